@@ -1,0 +1,168 @@
+/*
+ * fa.h - C ABI of libfa.so: exact scaled-dot-product attention on MI355X (gfx950).
+ *
+ * Two operations sit behind this interface.
+ *
+ *   fa_fwd           the attention forward pass computed FlashAttention-style:
+ *                    Q, K, V in device memory, O (and the per-row log-sum-exp)
+ *                    written back, the N x N score matrix never stored.
+ *   fa_paged_decode  one query token per sequence attending to a KV cache that
+ *                    is stored in fixed-size pages and reached through a block
+ *                    table.
+ *
+ * What is computed.  For every batch b and head h, with s_ij = scale * q_i . k_j
+ * over the keys j that query i may see (all j, or j <= i when causal):
+ *     o_i   = sum_j exp(s_ij) v_j / sum_j exp(s_ij)
+ *     lse_i = ln sum_j exp(s_ij)                       (natural log)
+ * This is the textbook scaled dot-product attention ("LLM study notes",
+ * DEVOCEAN tech blog, section on the self-attention computation: dot-product
+ * similarity, division by the square root of the key dimension, softmax,
+ * weighting of V; "Flash Attention", velog @myungum, section 1).  The method
+ * computes it exactly ("Flash Attention", velog @myungum, section 2: exact
+ * attention with far fewer memory accesses), so results differ from the plain
+ * definition only by floating-point rounding.
+ *
+ * Conventions shared by every entry point.
+ *   - Pointers are DEVICE pointers (HBM) unless stated otherwise.  The caller
+ *     owns every buffer; the library never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued on it and the call returns at once; results are valid after
+ *     the stream has been synchronised.
+ *   - Every array is row-major and densely packed.
+ *   - Errors are reported by the return value only.  Anything that can be
+ *     checked on the host is checked BEFORE any work is enqueued: a call that
+ *     returns FA_ERR_INVALID or FA_ERR_UNSUPPORTED has launched nothing and
+ *     written nothing.  FA_ERR_UNSUPPORTED means "valid request, no kernel for
+ *     it here": a caller may fall back to another implementation, as the fast
+ *     attention path in PyTorch does when head size, dtype, mask or hardware is
+ *     not supported ("How does Flash Attention reduce memory traffic in local
+ *     inference?", ZimaSpace blog, section on hardware and shape support).
+ *   - FA_ERR_HIP means a HIP call (a launch) failed; fa_last_hip_error() gives
+ *     the hipError_t of the last such failure on the calling thread.  Faults
+ *     during execution surface at stream synchronisation, as usual in HIP.
+ *   - Calls are deterministic: the same inputs give bit-identical outputs.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID = 1,      /* malformed arguments (null pointer, size < 1, non-finite scale, ...) */
+    FA_ERR_UNSUPPORTED = 2,  /* well-formed, but no kernel for this head size / dtype / page size */
+    FA_ERR_HIP = 3           /* a HIP runtime call failed; see fa_last_hip_error() */
+} fa_status;
+
+typedef enum {
+    FA_BF16 = 0,             /* bfloat16 inputs and outputs, float32 accumulation */
+    FA_F32 = 1               /* float32 inputs and outputs, float32 accumulation */
+} fa_dtype;
+
+/*
+ * fa_fwd - attention forward pass, one kernel launch.
+ *
+ * Follows "Flash Attention" (velog @myungum), section 2 and its pseudocode:
+ * Q, K, V split into row blocks staged through on-chip memory, scores computed
+ * per block, a running row max m and row sum l rescale the partial output as
+ * new key blocks arrive, so only O (and the row statistics) reach HBM.  Work is
+ * split over batch, heads and blocks of query rows, and each work group owns
+ * its rows of O ("FlashAttention-2 GPU work partitioning", iPLEX blog,
+ * section 3, changes 2 and 3).  The optional causal mask lets query i see keys
+ * j <= i only (same page, section 4).
+ *
+ *   q, k, v   [B][H][N][d] elements of `dtype`           (read)
+ *   o         [B][H][N][d] elements of `dtype`           (written; must not alias q, k, v)
+ *   lse       [B][H][N] float32, natural-log log-sum-exp of the scaled scores
+ *             of each row (written), or NULL to skip it
+ *   B, H, N   batch, heads, sequence length; each >= 1 (any N, not only
+ *             multiples of the tile size)
+ *   d         head dimension: 64 or 128 (else FA_ERR_UNSUPPORTED)
+ *   causal    0 = every query sees every key; 1 = query i sees keys 0..i
+ *   scale     multiplies q.k before the softmax; must be finite
+ *             (1/sqrt(d) is the textbook choice)
+ *   dtype     FA_BF16 or FA_F32 (a fa_dtype value)
+ *   stream    hipStream_t, or NULL
+ *
+ * Returns FA_OK, FA_ERR_INVALID (null q/k/v/o, B/H/N < 1, causal not 0/1,
+ * non-finite scale, B*H*N*d beyond 2^62), FA_ERR_UNSUPPORTED (d not 64/128,
+ * unknown dtype), or FA_ERR_HIP.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale,
+                 int dtype, void* stream);
+
+/*
+ * fa_paged_decode_workspace_size - bytes of device workspace fa_paged_decode
+ * needs for these sizes (0 if the sizes are invalid).  Host-only, no HIP call.
+ */
+size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int page_size,
+                                      int max_blocks_per_seq);
+
+/*
+ * fa_paged_decode - one query token per sequence against a paged KV cache.
+ *
+ * The KV cache is stored in fixed-size blocks ("pages") of `page_size` tokens;
+ * a per-sequence block table maps the logically contiguous token positions of a
+ * sequence onto physically scattered pages, and sequences may share pages
+ * (a common prompt prefix) simply by listing the same physical ids ("LLM study
+ * notes", DEVOCEAN tech blog, section "Paged attention": block table, at most
+ * block-size minus one wasted slots per sequence, prompt sharing).  The query
+ * attends to all seq_lens[s] cached tokens of its sequence (no mask).  The
+ * keys of one sequence are split into chunks worked on by separate work
+ * groups; a second small kernel merges the chunk results with the
+ * online-softmax rescaling rule ("Flash Attention", velog @myungum,
+ * pseudocode).
+ *
+ *   q            [S][H][d] elements of `dtype`              (read)
+ *   k_cache      [num_blocks][H][page_size][d] of `dtype`    (read)
+ *   v_cache      [num_blocks][H][page_size][d] of `dtype`    (read)
+ *   block_table  [S][max_blocks_per_seq] int32, physical page ids (read)
+ *   seq_lens     [S] int32, tokens cached per sequence       (read)
+ *   o            [S][H][d] elements of `dtype`              (written)
+ *   lse          [S][H] float32 natural-log log-sum-exp, or NULL
+ *   num_seqs (S), H >= 1;  d: 128 (else FA_ERR_UNSUPPORTED);
+ *   page_size: 16 (else FA_ERR_UNSUPPORTED);  max_blocks_per_seq >= 1;
+ *   num_blocks >= 1;  scale finite;  dtype: FA_BF16 (FA_F32 -> UNSUPPORTED)
+ *   workspace    device scratch of at least
+ *                fa_paged_decode_workspace_size(S, H, d, page_size, max_blocks_per_seq)
+ *                bytes, owned by the caller; contents on entry do not matter;
+ *                it must not be shared with a call still running on another
+ *                stream.
+ *
+ * Device-resident inputs are not inspected on the host (that would need a
+ * synchronisation).  Their out-of-range values have defined results instead:
+ *   seq_lens[s] <= 0        -> o[s] = 0 and lse[s] = -inf (empty softmax)
+ *   seq_lens[s] > max_blocks_per_seq * page_size -> clamped to that many tokens
+ *   a block_table entry outside [0, num_blocks) -> that page is skipped
+ *   table entries past page ceil(seq_lens[s]/page_size)-1, and cache slots
+ *   past seq_lens[s] in the last page, are never read.
+ *
+ * Returns FA_OK, FA_ERR_INVALID (null required pointer, sizes < 1, non-finite
+ * scale, workspace NULL or too small), FA_ERR_UNSUPPORTED, or FA_ERR_HIP.
+ */
+fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          void* o, float* lse,
+                          int num_seqs, int H, int d, int page_size,
+                          int max_blocks_per_seq, int64_t num_blocks, float scale,
+                          int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+/* hipError_t of the last FA_ERR_HIP returned on the calling thread (0 if none). */
+int fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

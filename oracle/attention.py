@@ -1,0 +1,169 @@
+"""CPU oracle for exact attention -- TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module.  It shares no code with the HIP
+path (``exact_attention_26_amd/``) and imports nothing from it.
+
+Everything is computed in float64 with numpy, straight from the definition,
+materialising the score matrix (one block of query rows at a time, which only
+bounds memory and does not change the arithmetic):
+
+    S = scale * Q K^T                      (similarity = dot product, scaled)
+    S_ij = -inf where key j is hidden      (causal: j > i)
+    m_i = max_j S_ij,  P = exp(S - m),  l_i = sum_j P_ij
+    O = (P V) / l,     LSE_i = m_i + ln l_i
+
+Sources: "LLM study notes" (DEVOCEAN tech blog), section on the self-attention
+computation (Q/K/V, dot-product similarity, division by the square root of the
+key dimension, softmax, weighting of the values); "Flash Attention" (velog
+@myungum), section 1 (scaled dot-product attention, several heads side by
+side) and section 2 (the method computes exact attention, so its result is this
+definition up to rounding); "How does Flash Attention reduce memory traffic in
+local inference?" (ZimaSpace blog), section on standard attention (the naive
+form that stores the full score matrix -- which is what this oracle is).  The
+causal mask is the one of "FlashAttention-2 GPU work partitioning" (iPLEX blog,
+section 4): a query sees the current and earlier tokens.  Paged decode follows
+"LLM study notes", section "Paged attention": a block table maps each
+sequence's logical pages to physical pages of the cache.
+
+Readings where the pages are silent (all pinned by tests in tests/test_oracle.py):
+  * the scale multiplies Q K^T before the max and the exponential;
+  * LSE is the natural log of sum_j exp(S_ij), with S already scaled;
+  * causal is square with no offset: query i sees keys 0..i;
+  * decode: the single query of a sequence sees all of its seq_len cached
+    tokens; seq_len <= 0 gives O = 0 and LSE = -inf (the empty sum).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = ["attention_fp64", "attention_bruteforce", "paged_gather_fp64", "paged_decode_fp64"]
+
+
+def _as64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention_fp64(q, k, v, *, causal: bool = False, scale: float | None = None,
+                   rows=None, row_block: int = 256):
+    """Exact attention in float64.
+
+    q: ``[..., Nq, d]``, k and v: ``[..., Nk, d]`` (same leading dims).  With
+    ``causal`` the mask is square (``Nq == Nk``) and query i sees keys
+    ``0..i``.  ``rows`` optionally selects query rows (indices into Nq); the
+    result then has ``len(rows)`` rows and each row is exactly the row the full
+    call would give.  ``scale`` defaults to ``1/sqrt(d)``.
+
+    Returns ``(o [..., R, d], lse [..., R])`` as float64.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    *lead, nq, d = q.shape
+    nk = k.shape[-2]
+    if k.shape[:-2] != tuple(lead) or v.shape[:-2] != tuple(lead) or k.shape[-1] != d \
+            or v.shape[-2] != nk:
+        raise ValueError("q, k, v shapes do not agree")
+    if causal and nq != nk:
+        raise ValueError("causal attention here is square (Nq == Nk)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    g = int(np.prod(lead)) if lead else 1
+    qf = q.reshape(g, nq, d)
+    kf = k.reshape(g, nk, d)
+    vf = v.reshape(g, nk, v.shape[-1])
+    o = np.empty((g, rows.size, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((g, rows.size), dtype=np.float64)
+    keys = np.arange(nk)
+    for gi in range(g):
+        for r0 in range(0, rows.size, row_block):
+            rr = rows[r0:r0 + row_block]
+            s = scale * (qf[gi, rr, :] @ kf[gi].T)              # [r, nk]
+            if causal:
+                s = np.where(keys[None, :] > rr[:, None], -np.inf, s)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            o[gi, r0:r0 + rr.size] = (p @ vf[gi]) / l
+            lse[gi, r0:r0 + rr.size] = (m + np.log(l))[:, 0]
+    return o.reshape(*lead, rows.size, v.shape[-1]), lse.reshape(*lead, rows.size)
+
+
+def attention_bruteforce(q, k, v, *, causal: bool = False, scale: float | None = None):
+    """Scalar loops over Python floats, for tiny inputs (N <= 16).
+
+    For one head: ``q [Nq][d]``, ``k [Nk][d]``, ``v [Nk][dv]`` as nested
+    sequences.  Uses the softmax exactly as defined, exp(s_ij) / sum_j exp(s_ij)
+    with no max subtraction (so keep |s| well below 700), and ``math.fsum`` for
+    the sums.  Returns ``(o, lse)`` as nested lists.
+    """
+    q = [[float(x) for x in row] for row in q]
+    k = [[float(x) for x in row] for row in k]
+    v = [[float(x) for x in row] for row in v]
+    d = len(q[0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o, lse = [], []
+    for i, qi in enumerate(q):
+        seen = [j for j in range(len(k)) if not (causal and j > i)]
+        w = [math.exp(scale * math.fsum(a * b for a, b in zip(qi, k[j]))) for j in seen]
+        z = math.fsum(w)
+        o.append([math.fsum(w[t] * v[j][c] for t, j in enumerate(seen)) / z
+                  for c in range(len(v[0]))])
+        lse.append(math.log(z))
+    return o, lse
+
+
+def paged_gather_fp64(k_cache, v_cache, block_table, seq_len: int, seq: int, head: int):
+    """Logical K and V rows ``[L][d]`` of one (sequence, head), read through the table.
+
+    Logical page p of the sequence holds tokens ``p*page_size ..
+    p*page_size + page_size - 1`` and lives in physical page
+    ``block_table[seq][p]`` of a ``[num_blocks][H][page_size][d]`` cache.
+    Only the first ``seq_len`` tokens are returned (slots past the end of the
+    last page are never touched).
+    """
+    page_size = k_cache.shape[2]
+    n_pages = -(-seq_len // page_size)
+    if n_pages > block_table.shape[1]:
+        raise ValueError("seq_len exceeds the block table")
+    ks, vs = [], []
+    for p in range(n_pages):
+        blk = int(block_table[seq][p])
+        take = min(page_size, seq_len - p * page_size)
+        ks.append(_as64(k_cache[blk, head, :take, :]))
+        vs.append(_as64(v_cache[blk, head, :take, :]))
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def paged_decode_fp64(q, k_cache, v_cache, block_table, seq_lens, *, scale: float | None = None,
+                      pairs=None):
+    """One query per sequence against a paged KV cache, float64.
+
+    q: ``[S][H][d]``; caches ``[num_blocks][H][page_size][d]``; block_table
+    ``[S][max_blocks]``; seq_lens ``[S]``.  The query of sequence s sees all of
+    its ``seq_lens[s]`` tokens.  ``pairs`` optionally lists ``(s, h)`` to
+    compute; the result then holds those entries in order.
+
+    Returns ``(o, lse)``: ``[S][H][d]`` and ``[S][H]`` (or ``[len(pairs)][d]``
+    and ``[len(pairs)]``).  ``seq_lens[s] <= 0`` gives ``o = 0``,
+    ``lse = -inf``.
+    """
+    S, H, d = np.shape(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    want = [(s, h) for s in range(S) for h in range(H)] if pairs is None else list(pairs)
+    o = np.zeros((len(want), d), dtype=np.float64)
+    lse = np.full(len(want), -np.inf, dtype=np.float64)
+    for n, (s, h) in enumerate(want):
+        L = int(seq_lens[s])
+        if L <= 0:
+            continue
+        ks, vs = paged_gather_fp64(k_cache, v_cache, block_table, L, s, h)
+        oo, ll = attention_fp64(_as64(q[s, h])[None, :], ks, vs, causal=False, scale=scale)
+        o[n] = oo[0]
+        lse[n] = ll[0]
+    if pairs is None:
+        return o.reshape(S, H, d), lse.reshape(S, H)
+    return o, lse
