@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input, resident in HBM:
+  * forward, B=8 H=16 N=2048 d=128 bf16, non-causal        (fa_fwd)
+  * forward, same inputs, causal                           (fa_fwd)
+  * paged-KV decode, 64 sequences of 128..8192 tokens, H=32, d=128, pages of 16,
+    shuffled pool, pairs sharing a 512-token prefix        (fa_paged_decode)
+
+`value` is the forward throughput in TFLOP/s (algorithmic FLOPs of the two
+forward calls over their kernel time, HIP events on the launch stream).  The
+decode's HBM GB/s, per-call figures, the roofline of the dominant kernel and
+the CPU oracle's rate on a bounded sample are reported in the same JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0           # HBM3E, 8 TB/s
+METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak; paged decode HBM GB/s (1 GPU)"
+
+
+def fwd_flops(B, H, N, d, causal):
+    """Algorithmic FLOPs: 4*N^2*d per head (2 for QK^T, 2 for PV); causal counts
+    only the N(N+1)/2 visible pairs.  Masked work and exponentials not counted."""
+    return 2.0 * B * H * d * N * (N + 1) if causal else 4.0 * B * H * N * N * d
+
+
+def decode_bytes(layout):
+    """Algorithmic HBM bytes of one decode call: every K/V row a query must see,
+    each distinct physical (page, head) row once, plus q, o, lse, the used
+    table entries and seq_lens."""
+    from exact_attention_26_amd.workloads import page_valid_slots
+    valid = page_valid_slots(layout)
+    kv = float(valid.sum()) * layout.H * layout.d * 2 * 2
+    logical = float(np.maximum(layout.seq_lens, 0).sum()) * layout.H * layout.d * 2 * 2
+    pages_used = sum(layout.used_pages(s).size for s in range(layout.S))
+    small = layout.S * layout.H * layout.d * 2 * 2 + layout.S * layout.H * 4 + pages_used * 4 \
+        + layout.S * 4
+    return kv + small, logical + small
+
+
+def cpu_baseline(budget_s: float = 15.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the forward
+    workload: whole (b, h) heads of the non-causal B=8 H=16 N=2048 d=128
+    problem, one after another until the time budget is used."""
+    from exact_attention_26_amd import workloads as w
+    from oracle import attention_fp64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = None
+    cfg = w.FWD_CONFIGS["fwd_b8_h16_n2048_d128"]
+    q, k, v = w.fwd_config_inputs(cfg)
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            attention_fp64(q[b, h], k[b, h], v[b, h], causal=False, scale=cfg.scale)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = fwd_flops(1, done, cfg.N, cfg.d, False)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.B * cfg.H} (b,h) heads of the non-causal forward "
+                      f"B=8 H=16 N=2048 d=128, fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true",
+                    help="forward only (for profiling the forward kernel alone)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are "
+              "single-GPU and no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_26_amd as fa
+    from exact_attention_26_amd import workloads as w
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+
+    # ---- forward inputs ----
+    cfg = w.FWD_CONFIGS["fwd_b8_h16_n2048_d128"]
+    q, k, v = w.fwd_config_inputs(cfg)
+    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    del q, k, v
+    o_nc = torch.empty_like(qd)
+    o_c = torch.empty_like(qd)
+    lse_nc = torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
+    lse_c = torch.empty_like(lse_nc)
+    log("forward inputs ready")
+
+    # ---- decode inputs ----
+    decode = not args.skip_decode
+    if decode:
+        L = w.decode_layout(**w.DECODE_C4)
+        qdec = torch.from_numpy(w.decode_q(L)).to(dev).to(torch.bfloat16)
+        pools = []
+        for which in ("k", "v"):
+            pool = torch.empty((L.num_blocks, L.H, L.page_size, L.d), dtype=torch.bfloat16,
+                               device=dev)
+
+            def put(lo, hi, x, pool=pool):
+                pool[lo:hi].copy_(torch.from_numpy(x).to(dev))
+            w.decode_pool(L, which, poison=False, chunk_callback=put)
+            pools.append(pool)
+        kc, vc = pools
+        bt = torch.from_numpy(L.block_table).to(dev)
+        sl = torch.from_numpy(L.seq_lens).to(dev)
+        ws = torch.empty(fa.fa_paged_decode_workspace_size(L.S, L.H, L.d, L.page_size,
+                                                            L.max_blocks),
+                         dtype=torch.uint8, device=dev)
+        o_dec = torch.empty_like(qdec)
+        lse_dec = torch.empty((L.S, L.H), dtype=torch.float32, device=dev)
+        dec_bytes, dec_logical = decode_bytes(L)
+        log(f"decode inputs ready: {L.num_blocks} pages, sum L = {int(L.seq_lens.sum())}")
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(timed, acc):
+        ev[0].record(stream)
+        fa.fa_fwd(qd, kd, vd, o_nc, lse_nc, False, cfg.scale)
+        ev[1].record(stream)
+        fa.fa_fwd(qd, kd, vd, o_c, lse_c, True, cfg.scale)
+        ev[2].record(stream)
+        if decode:
+            fa.fa_paged_decode(qdec, kc, vc, bt, sl, o_dec, lse_dec, L.scale, ws)
+        ev[3].record(stream)
+        if timed:
+            ev[3].synchronize()
+            acc[0] += ev[0].elapsed_time(ev[1])
+            acc[1] += ev[1].elapsed_time(ev[2])
+            acc[2] += ev[2].elapsed_time(ev[3])
+
+    for _ in range(args.warmup):
+        step(False, None)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # whole-step wall time (no per-call syncs inside)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False, None)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-call kernel times from HIP events on the launch stream
+    acc = [0.0, 0.0, 0.0]
+    for _ in range(args.steps):
+        step(True, acc)
+    torch.cuda.synchronize()
+    t_nc, t_c, t_dec = (a / args.steps for a in acc)
+    log("timed steps done")
+
+    f_nc = fwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, False)
+    f_c = fwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, True)
+    tflops_nc = f_nc / (t_nc * 1e-3) / 1e12
+    tflops_c = f_c / (t_c * 1e-3) / 1e12
+    value = (f_nc + f_c) / ((t_nc + t_c) * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention forward B=8 H=16 N=2048 d=128 bf16 (non-causal + causal)"
+                               + (" + paged-KV decode S=64 H=32 d=128 page=16 L=128..8192"
+                                  if decode else ""),
+                   "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.d,
+                   "parallelism": "single GPU"},
+        "fwd": {"noncausal_ms": round(t_nc, 4), "noncausal_tflops": round(tflops_nc, 2),
+                "noncausal_frac_peak": round(tflops_nc / PEAK_BF16_TFLOPS, 4),
+                "causal_ms": round(t_c, 4), "causal_tflops": round(tflops_c, 2),
+                "causal_frac_peak": round(tflops_c / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops_nc, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops_nc / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fwd_kernel<bf16,128,non-causal>",
+                     "flops_per_launch": f_nc},
+    }
+    if decode:
+        gbs = dec_bytes / (t_dec * 1e-3) / 1e9
+        out["decode"] = {"ms": round(t_dec, 4), "hbm_gbs": round(gbs, 1),
+                         "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": dec_bytes, "logical_bytes": dec_logical,
+                         "logical_gbs": round(dec_logical / (t_dec * 1e-3) / 1e9, 1)}
+        out["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs, 1),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

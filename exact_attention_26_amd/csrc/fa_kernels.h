@@ -1,0 +1,16 @@
+// fa_kernels.h - launchers of the gfx950 kernels, called by the C ABI (fa_api.cpp).
+// Arguments have already been validated by fa_validate.h when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+hipError_t fa_launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int N, int d, int causal, float scale, int dtype,
+                         hipStream_t stream);
+
+hipError_t fa_launch_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  void* o, float* lse, int S, int H, int d,
+                                  int max_blocks, int64_t num_blocks, float scale,
+                                  float* workspace, hipStream_t stream);

@@ -1,0 +1,86 @@
+// fa_validate.h - host-side argument checks of the C ABI (include/fa.h).
+//
+// Pure C++17, no HIP: the same checks are compiled into libfa.so and into a
+// host-only unit test built with g++.  Every check here runs before anything is
+// enqueued, so a call rejected here has launched nothing.
+#pragma once
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "fa.h"
+
+namespace fa_host {
+
+// Forward pass: query rows per work group.
+constexpr int kFwdBlockM = 128;
+// Paged decode: pages of one sequence handled by one work group.
+constexpr int kDecodeSplitPages = 32;
+// Paged decode: the one page size the kernels are built for.
+constexpr int kDecodePageSize = 16;
+
+inline bool fwd_head_dim_supported(int d) { return d == 64 || d == 128; }
+inline bool decode_head_dim_supported(int d) { return d == 64 || d == 128; }
+
+inline fa_status check_fwd(const void* q, const void* k, const void* v, const void* o,
+                           int B, int H, int N, int d, int causal, float scale, int dtype) {
+    if (!q || !k || !v || !o) return FA_ERR_INVALID;
+    if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID;
+    const double elems = double(B) * double(H) * double(N) * double(d);
+    if (elems >= 4611686018427387904.0) return FA_ERR_INVALID;           // 2^62
+    // one work group per (b, h, block of query rows): the 1-D grid must fit
+    const double groups = double(B) * double(H) * std::ceil(double(N) / kFwdBlockM);
+    if (groups > 2147483647.0) return FA_ERR_INVALID;
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+    if (!fwd_head_dim_supported(d)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+inline int decode_max_splits(int max_blocks_per_seq) {
+    return (max_blocks_per_seq + kDecodeSplitPages - 1) / kDecodeSplitPages;
+}
+
+// Workspace: per (sequence, head, split) one partial result of d + 2 floats
+// (running max, running sum, unnormalised output row).  0 = invalid sizes.
+inline size_t decode_workspace_bytes(int S, int H, int d, int page_size, int max_blocks) {
+    if (S < 1 || H < 1 || d < 1 || page_size < 1 || max_blocks < 1) return 0;
+    const double bytes = double(S) * H * decode_max_splits(max_blocks) * (double(d) + 2.0) * 4.0;
+    if (bytes > 1.0e15) return 0;
+    return size_t(S) * size_t(H) * size_t(decode_max_splits(max_blocks)) * (size_t(d) + 2) * 4;
+}
+
+inline fa_status check_decode(const void* q, const void* kc, const void* vc, const void* table,
+                              const void* lens, const void* o, int S, int H, int d,
+                              int page_size, int max_blocks, int64_t num_blocks, float scale,
+                              int dtype, const void* ws, size_t ws_bytes) {
+    if (!q || !kc || !vc || !table || !lens || !o) return FA_ERR_INVALID;
+    if (S < 1 || H < 1 || d < 1 || page_size < 1 || max_blocks < 1 || num_blocks < 1)
+        return FA_ERR_INVALID;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID;
+    if (S > 65535 || H > 65535) return FA_ERR_INVALID;                   // grid y/z limits
+    const double pool = double(num_blocks) * H * page_size * d;
+    if (pool >= 4611686018427387904.0) return FA_ERR_INVALID;
+    if (double(S) * max_blocks >= 2147483647.0) return FA_ERR_INVALID;   // int32 table index
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!decode_head_dim_supported(d)) return FA_ERR_UNSUPPORTED;
+    if (page_size != kDecodePageSize) return FA_ERR_UNSUPPORTED;
+    const size_t need = decode_workspace_bytes(S, H, d, page_size, max_blocks);
+    if (need == 0 || !ws || ws_bytes < need) return FA_ERR_INVALID;
+    return FA_OK;
+}
+
+inline const char* status_string(int s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this configuration";
+        case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";
+        default: return "unknown fa_status";
+    }
+}
+
+}  // namespace fa_host

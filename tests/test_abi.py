@@ -1,0 +1,115 @@
+"""The C-ABI library on the CPU: it loads, exports what include/fa.h declares,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import exact_attention_26_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted([
+        "fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_status_string",
+        "fa_last_hip_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", fa.library_path()],
+                             capture_output=True, text=True, check=True).stdout
+        exported = set(re.findall(r" T (fa_\w+)", out))
+        assert set(_declared_functions()) <= exported
+
+
+def test_status_strings_and_last_error():
+    assert fa.fa_status_string(0) == "FA_OK"
+    assert "INVALID" in fa.fa_status_string(1)
+    assert "UNSUPPORTED" in fa.fa_status_string(2)
+    assert "HIP" in fa.fa_status_string(3)
+    assert "unknown" in fa.fa_status_string(42)
+    assert fa.fa_last_hip_error() == 0
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=1, N=16, d=64, causal=0,
+             scale=0.125, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.load_library().fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                    a["N"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 1), (dict(H=0), 1), (dict(N=0), 1), (dict(N=-3), 1), (dict(causal=3), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+    (dict(d=96), 2), (dict(d=32), 2), (dict(d=256), 2), (dict(dtype=5), 2),
+])
+def test_fwd_rejects_before_launch(kw, status):
+    assert _fwd(**kw) == status
+
+
+def test_decode_workspace_size():
+    assert fa.fa_paged_decode_workspace_size(64, 32, 128, 16, 512) == 64 * 32 * 16 * 130 * 4
+    assert fa.fa_paged_decode_workspace_size(3, 2, 64, 16, 33) == 3 * 2 * 2 * 66 * 4
+    assert fa.fa_paged_decode_workspace_size(0, 2, 64, 16, 33) == 0
+
+
+def _decode(**kw):
+    ws = fa.fa_paged_decode_workspace_size(2, 2, 128, 16, 4)
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=None, S=2, H=2, d=128,
+             P=16, mb=4, nb=10, scale=0.1, dtype=fa.FA_BF16, ws=FAKE, wsb=ws)
+    a.update(kw)
+    return fa.load_library().fa_paged_decode(
+        a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"], a["lse"], a["S"], a["H"], a["d"],
+        a["P"], a["mb"], a["nb"], a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(bt=None), 1),
+    (dict(sl=None), 1), (dict(o=None), 1), (dict(S=0), 1), (dict(H=0), 1), (dict(mb=0), 1),
+    (dict(nb=0), 1), (dict(scale=float("nan")), 1), (dict(ws=None), 1), (dict(wsb=16), 1),
+    (dict(d=96), 2), (dict(P=8), 2), (dict(dtype=fa.FA_F32), 2), (dict(dtype=9), 2),
+])
+def test_decode_rejects_before_launch(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_host_validation_unit_with_sanitizers(tmp_path):
+    """The validation header on its own, compiled with g++ (no HIP) under ASan/UBSan."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = tmp_path / "test_validate"
+    subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-I" + os.path.join(ROOT, "include"),
+                    "-I" + os.path.join(ROOT, "exact_attention_26_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "host", "test_validate.cpp"), "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    import exact_attention_26_amd._binding as b
+    monkeypatch.setattr(b, "_LIB", None)
+    monkeypatch.setenv("FA_LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(fa.FaError):
+        b.load_library()
