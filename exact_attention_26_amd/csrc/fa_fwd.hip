@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_kernels.h"
 
 namespace {
@@ -81,6 +83,13 @@ __device__ __forceinline__ uint32_t bf16_bits(const u32x4& v, int e) {
     return (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
 }
 
+// Largest growth of the running maximum (in log2 units) absorbed without
+// rescaling: the accumulator is rescaled only when a row's maximum grows by
+// more than this, so probabilities stay below 2^8 and the usual case (maximum
+// unchanged or barely changed) costs no rescale at all.  The result is the
+// same: O, l and m always refer to one common reference maximum.
+constexpr float kRescaleThreshold = 8.0f;
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2)
 void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -95,8 +104,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     constexpr int CPR = D / VEC;               // 16-byte vectors per row
     constexpr int NV = BN * CPR / NTHREADS;    // consecutive rows per thread per tile
     constexpr int KS = D + VEC;                // K row stride in LDS (16-byte pad)
-    constexpr int VPAD = (sizeof(T) == 2) ? 4 : 4;
-    constexpr int VS = BN + VPAD;              // V^T row stride in LDS
+    constexpr int VS = BN + 4;                 // V^T row stride in LDS
     constexpr int ND = D / 32;                 // 32-row blocks of O^T
     constexpr int NCH = 32 / KC;               // PV MFMAs per 32-key block
     static_assert(NV * NTHREADS == BN * CPR, "tile does not split evenly over threads");
@@ -129,6 +137,13 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int wq0 = q0 + wave * 32;            // first query row of this wave
     const int qrow = wq0 + l32;                // this lane's query row
 
+    // Scores are kept raw (q.k) and scaled inside the exponent:
+    // p = 2^(c*s - c*m) with c = |scale| * log2(e).  A negative scale is folded
+    // into Q by flipping its sign bits, which is exact.
+    const float c = fabsf(scale_log2);
+    const bool neg = scale_log2 < 0.f;
+    const float tau_raw = (c > 0.f) ? kRescaleThreshold / c : __builtin_inff();
+
     // Q fragment of this lane: B operand of S^T = K Q^T, kept in registers.
     op_t qop[NKC];
 #pragma unroll
@@ -136,9 +151,11 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         if constexpr (E == 8) {
             u32x4 x = {0u, 0u, 0u, 0u};
             if (qrow < N) x = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + kc * KC + g * E);
+            if (neg) x ^= 0x80008000u;
             qop[kc] = __builtin_bit_cast(bf16x8, x);
         } else {
-            qop[kc] = (qrow < N) ? Qh[(size_t)qrow * D + kc * KC + g] : 0.f;
+            const float x = (qrow < N) ? Qh[(size_t)qrow * D + kc * KC + g] : 0.f;
+            qop[kc] = neg ? -x : x;
         }
     }
 
@@ -147,11 +164,13 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_run = kNegInf;
-    float l_run = 0.f;
+    float m_run = kNegInf;                     // running max of raw scores
+    float l_run = 0.f;                         // this lane's share of the row sum
 
     const int n_kt_all = (N + BN - 1) / BN;
     const int n_kt = CAUSAL ? min(n_kt_all, (q0 + BM + BN - 1) / BN) : n_kt_all;
+    // tiles before n_full need no mask for any row of this work group
+    const int n_full = CAUSAL ? min(N / BN, q0 / BN) : N / BN;
 
     // global -> register staging of one K/V tile: thread owns NV consecutive rows
     // of one 16-byte column chunk (so it can store V transposed NV keys at a time).
@@ -159,22 +178,30 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int vrow0 = (tid / CPR) * NV;
     u32x4 kreg[NV], vreg[NV];
     auto gload = [&](int kt) {
+        const int row0 = kt * BN + vrow0;
+        const T* kp = Kh + (size_t)row0 * D + vchunk * VEC;
+        const T* vp = Vh + (size_t)row0 * D + vchunk * VEC;
+        if (kt * BN + BN <= N) {
 #pragma unroll
-        for (int r = 0; r < NV; ++r) {
-            const int row = kt * BN + vrow0 + r;
-            u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-            if (row < N) {
-                kx = *reinterpret_cast<const u32x4*>(Kh + (size_t)row * D + vchunk * VEC);
-                vx = *reinterpret_cast<const u32x4*>(Vh + (size_t)row * D + vchunk * VEC);
+            for (int r = 0; r < NV; ++r) {
+                kreg[r] = *reinterpret_cast<const u32x4*>(kp + r * D);
+                vreg[r] = *reinterpret_cast<const u32x4*>(vp + r * D);
             }
-            kreg[r] = kx;
-            vreg[r] = vx;
+        } else {
+#pragma unroll
+            for (int r = 0; r < NV; ++r) {
+                u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+                if (row0 + r < N) {
+                    kx = *reinterpret_cast<const u32x4*>(kp + r * D);
+                    vx = *reinterpret_cast<const u32x4*>(vp + r * D);
+                }
+                kreg[r] = kx;
+                vreg[r] = vx;
+            }
         }
     };
-    gload(0);
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        __syncthreads();                       // every wave is done with the previous tile
+    auto stage = [&]() {
 #pragma unroll
         for (int r = 0; r < NV; ++r)
             *reinterpret_cast<u32x4*>(&Ks[(vrow0 + r) * KS + vchunk * VEC]) = kreg[r];
@@ -182,13 +209,17 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         for (int e = 0; e < VEC; ++e) {
             T* dst = &Vt[(vchunk * VEC + e) * VS + vrow0];
             if constexpr (sizeof(T) == 2) {
+                // pack element e of consecutive rows: low halves (even e) or
+                // high halves (odd e) of word e/2, two rows per 32-bit word
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                const int wd = e >> 1;
                 if constexpr (NV == 4) {
-                    u32x2 w = {bf16_bits(vreg[0], e) | (bf16_bits(vreg[1], e) << 16),
-                               bf16_bits(vreg[2], e) | (bf16_bits(vreg[3], e) << 16)};
+                    u32x2 w = {__builtin_amdgcn_perm(vreg[1][wd], vreg[0][wd], sel),
+                               __builtin_amdgcn_perm(vreg[3][wd], vreg[2][wd], sel)};
                     *reinterpret_cast<u32x2*>(dst) = w;
                 } else {
                     *reinterpret_cast<uint32_t*>(dst) =
-                        bf16_bits(vreg[0], e) | (bf16_bits(vreg[1], e) << 16);
+                        __builtin_amdgcn_perm(vreg[1][wd], vreg[0][wd], sel);
                 }
             } else {
 #pragma unroll
@@ -199,12 +230,12 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                 }
             }
         }
-        __syncthreads();
-        if (kt + 1 < n_kt) gload(kt + 1);      // next tile in flight during compute
+    };
 
-        const int k0 = kt * BN;
-        if (CAUSAL && k0 > wq0 + 31) continue; // tile entirely above this wave's diagonal
-
+    // One key tile from LDS: scores, online softmax, PV.  MASK selects the
+    // variant that hides keys >= N and (causal) keys > query.
+    auto compute = [&](auto mask_tag, int k0) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         // ---- scores, transposed: sacc[kb] = K[k0+32kb .. +32] Q^T ----
         f32x16 sacc[2];
 #pragma unroll
@@ -220,70 +251,86 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                 sacc[kb] = EL::mma(a, qop[kc], sacc[kb]);
             }
         }
-
-        // ---- online softmax (log2 domain); lane holds query qrow, keys
-        //      k0 + 32kb + 8(r/4) + 4g + r%4 for r = 0..15 ----
-        const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > wq0);
+        // lane holds query qrow and keys k0 + 32kb + 8(r/4) + 4g + r%4, r = 0..15;
+        // hidden keys become -inf and are mapped to p = 0 below
         float mt = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = sacc[kb][r] * scale_log2;
-                if (need_mask) {
+                if constexpr (MASK) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= N || (CAUSAL && key > qrow)) x = kNegInf;
+                    if (key >= N || (CAUSAL && key > qrow)) sacc[kb][r] = kNegInf;
                 }
-                sacc[kb][r] = x;
-                mt = fmaxf(mt, x);
+                mt = fmaxf(mt, sacc[kb][r]);
             }
         mt = fmaxf(mt, xor32(mt));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.f;
+        // rescale only when some row's maximum grew past the threshold
+        if (__any(mt > m_run + tau_raw)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(sacc[kb][r] - m_use);
+                float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
+                if constexpr (MASK) p = (sacc[kb][r] == kNegInf) ? 0.f : p;
                 sacc[kb][r] = p;
-                psum += p;
+                if (r & 1) ps1 += p; else ps0 += p;
             }
-        l_run = l_run * alpha + psum;          // row sum from the fp32 probabilities
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        l_run += ps0 + ps1;                    // row sum from the fp32 probabilities
 
         // ---- O^T += V^T P^T ----
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
+            for (int cc = 0; cc < NCH; ++cc) {
                 op_t b;
                 if constexpr (E == 8) {
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) b[s] = (__bf16)sacc[kb][8 * c + s];
+                    for (int s2 = 0; s2 < 8; ++s2) b[s2] = (__bf16)sacc[kb][8 * cc + s2];
                 } else {
-                    b = sacc[kb][c];
+                    b = sacc[kb][cc];
                 }
 #pragma unroll
                 for (int db = 0; db < ND; ++db) {
                     const T* vrow = &Vt[(db * 32 + l32) * VS + kb * 32];
                     op_t a;
                     if constexpr (E == 8) {
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * c + 4 * g);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * c + 8 + 4 * g);
+                        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * cc + 4 * g);
+                        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * cc + 8 + 4 * g);
                         const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
                         a = __builtin_bit_cast(bf16x8, w);
                     } else {
-                        a = vrow[8 * (c >> 2) + 4 * g + (c & 3)];
+                        a = vrow[8 * (cc >> 2) + 4 * g + (cc & 3)];
                     }
                     oacc[db] = EL::mma(a, b, oacc[db]);
                 }
             }
+        }
+    };
+
+    gload(0);
+    for (int kt = 0; kt < n_kt; ++kt) {
+        __syncthreads();                       // every wave is done with the previous tile
+        stage();
+        __syncthreads();
+        if (kt + 1 < n_kt) gload(kt + 1);      // next tile in flight during compute
+        const int k0 = kt * BN;
+        if (kt < n_full) {
+            compute(std::integral_constant<bool, false>{}, k0);
+        } else {
+            if (CAUSAL && k0 > wq0 + 31) continue;   // tile entirely above this wave's diagonal
+            compute(std::integral_constant<bool, true>{}, k0);
         }
     }
 
@@ -309,8 +356,10 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                     *reinterpret_cast<f32x4*>(orow + d0) = w;
                 }
             }
-        if (LSE != nullptr && g == 0)
-            LSE[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        if (LSE != nullptr && g == 0) {
+            const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+            LSE[(size_t)bh * N + qrow] = (mc + __log2f(l_tot)) * kLn2;
+        }
     }
 }
 
