@@ -172,16 +172,23 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     // tiles before n_full need no mask for any row of this work group
     const int n_full = CAUSAL ? min(N / BN, q0 / BN) : N / BN;
 
-    // global -> register staging of one K/V tile: thread owns NV consecutive rows
-    // of one 16-byte column chunk (so it can store V transposed NV keys at a time).
-    const int vchunk = tid % CPR;
-    const int vrow0 = (tid / CPR) * NV;
+    // global -> register staging of one K/V tile.  K: thread owns NV
+    // consecutive rows of one 16-byte column chunk, consecutive threads take
+    // consecutive chunks (so a K row is stored as one contiguous LDS run).
+    // V: same ownership, but consecutive threads take consecutive groups of
+    // rows of one chunk, so the transposed store of a group of lanes fills one
+    // contiguous run of a V^T row (no LDS bank conflicts).
+    constexpr int RG = BN / NV;                // row groups per tile
+    const int kchunk = tid % CPR;
+    const int krow0 = (tid / CPR) * NV;
+    const int vchunk = tid / RG;
+    const int vrow0 = (tid % RG) * NV;
     u32x4 kreg[NV], vreg[NV];
     auto gload = [&](int kt) {
-        const int row0 = kt * BN + vrow0;
-        const T* kp = Kh + (size_t)row0 * D + vchunk * VEC;
-        const T* vp = Vh + (size_t)row0 * D + vchunk * VEC;
-        if (kt * BN + BN <= N) {
+        const int base_row = kt * BN;
+        const T* kp = Kh + (size_t)(base_row + krow0) * D + kchunk * VEC;
+        const T* vp = Vh + (size_t)(base_row + vrow0) * D + vchunk * VEC;
+        if (base_row + BN <= N) {
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
                 kreg[r] = *reinterpret_cast<const u32x4*>(kp + r * D);
@@ -191,10 +198,8 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
                 u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-                if (row0 + r < N) {
-                    kx = *reinterpret_cast<const u32x4*>(kp + r * D);
-                    vx = *reinterpret_cast<const u32x4*>(vp + r * D);
-                }
+                if (base_row + krow0 + r < N) kx = *reinterpret_cast<const u32x4*>(kp + r * D);
+                if (base_row + vrow0 + r < N) vx = *reinterpret_cast<const u32x4*>(vp + r * D);
                 kreg[r] = kx;
                 vreg[r] = vx;
             }
@@ -204,7 +209,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     auto stage = [&]() {
 #pragma unroll
         for (int r = 0; r < NV; ++r)
-            *reinterpret_cast<u32x4*>(&Ks[(vrow0 + r) * KS + vchunk * VEC]) = kreg[r];
+            *reinterpret_cast<u32x4*>(&Ks[(krow0 + r) * KS + kchunk * VEC]) = kreg[r];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             T* dst = &Vt[(vchunk * VEC + e) * VS + vrow0];
