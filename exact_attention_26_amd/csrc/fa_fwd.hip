@@ -324,19 +324,25 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         }
     };
 
+    // Two loops, one per tile variant, so each has a single compute body
+    // (one body per loop keeps the accumulators in place across iterations).
     gload(0);
-    for (int kt = 0; kt < n_kt; ++kt) {
+    int kt = 0;
+    for (; kt < n_full; ++kt) {
         __syncthreads();                       // every wave is done with the previous tile
         stage();
         __syncthreads();
         if (kt + 1 < n_kt) gload(kt + 1);      // next tile in flight during compute
+        compute(std::integral_constant<bool, false>{}, kt * BN);
+    }
+    for (; kt < n_kt; ++kt) {
+        __syncthreads();
+        stage();
+        __syncthreads();
+        if (kt + 1 < n_kt) gload(kt + 1);
         const int k0 = kt * BN;
-        if (kt < n_full) {
-            compute(std::integral_constant<bool, false>{}, k0);
-        } else {
-            if (CAUSAL && k0 > wq0 + 31) continue;   // tile entirely above this wave's diagonal
-            compute(std::integral_constant<bool, true>{}, k0);
-        }
+        if (CAUSAL && k0 > wq0 + 31) continue;   // tile entirely above this wave's diagonal
+        compute(std::integral_constant<bool, true>{}, k0);
     }
 
     // ---- epilogue: O = O_acc / l, LSE = ln(l) + m ----
