@@ -402,8 +402,7 @@ hipError_t fa_launch_fwd(const void* q, const void* k, const void* v, void* o, f
                          int B, int H, int N, int d, int causal, float scale, int dtype,
                          hipStream_t stream) {
     if (dtype == 0) {
-        if (d == 128) return launch_causal<__bf16, 128>(q, k, v, o, lse, B, H, N, causal, scale, stream);
-        if (d == 64) return launch_causal<__bf16, 64>(q, k, v, o, lse, B, H, N, causal, scale, stream);
+        return fa_launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream);
     } else {
         if (d == 128) return launch_causal<float, 128>(q, k, v, o, lse, B, H, N, causal, scale, stream);
         if (d == 64) return launch_causal<float, 64>(q, k, v, o, lse, B, H, N, causal, scale, stream);

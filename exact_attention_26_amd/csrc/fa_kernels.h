@@ -9,6 +9,11 @@ hipError_t fa_launch_fwd(const void* q, const void* k, const void* v, void* o, f
                          int B, int H, int N, int d, int causal, float scale, int dtype,
                          hipStream_t stream);
 
+// bf16 fast path (fa_fwd_bf16.hip)
+hipError_t fa_launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N, int d, int causal, float scale,
+                              hipStream_t stream);
+
 hipError_t fa_launch_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   void* o, float* lse, int S, int H, int d,
