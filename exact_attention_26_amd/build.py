@@ -25,9 +25,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I" + INCLUDE, "-I" + CSRC]
 
 
+# Per-source extra flags.  The bf16 forward keeps every MFMA accumulator in
+# VGPRs: its whole working set fits in 256 VGPRs at two waves per SIMD, and the
+# softmax reads the score accumulators with VALU instructions.
+EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
@@ -48,6 +54,12 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # a kernel whose host-side handle was not emitted shows up as an undefined
+    # symbol of this library's own (anonymous-namespace) code: refuse it
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "_GLOBAL__N_" in l]
+    if nm.returncode == 0 and missing:
+        raise RuntimeError(f"kernel handles missing from libfa.so: {missing}")
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")

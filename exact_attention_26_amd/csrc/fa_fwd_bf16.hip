@@ -16,8 +16,8 @@
 //  * K and V tiles (64 keys) go HBM -> LDS with global_load_lds_dwordx4 (no
 //    register staging), double-buffered: the next tile is in flight while the
 //    current one is computed, with one barrier per tile.  Rows are stored with
-//    their 16-byte chunks XOR-swizzled by the row index, which makes both the
-//    K reads and the transposed V reads below free of LDS bank conflicts.
+//    their 16-byte chunks XOR-swizzled by the row index (see swz), which makes
+//    both the K reads and the transposed V reads free of LDS bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
 //    Q held in registers as the B operand).  In that accumulator layout a lane
 //    holds one query and 16 keys, so row max / row sum are in-lane plus one
@@ -76,32 +76,46 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// acc *= alpha for an MFMA accumulator that lives in AGPRs.  Done in place
-// (read to a VGPR, multiply, write back) so the accumulator never has to move
-// to VGPRs; this is the rare rescale path, so the wait states are generous
-// (covers any MFMA still writing acc, and the next MFMA reading it).
+// acc *= alpha (the rare rescale path of the online softmax)
 __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        float x = acc[r];
-        float t;
-        asm volatile(
-            "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-            "v_accvgpr_read_b32 %1, %0\n\t"
-            "v_mul_f32 %1, %1, %2\n\t"
-            "v_accvgpr_write_b32 %0, %1\n\t"
-            "s_nop 7"
-            : "+a"(x), "=&v"(t)
-            : "v"(alpha));
-        acc[r] = x;
-    }
+    for (int r = 0; r < 16; ++r) acc[r] *= alpha;
 }
 
-// Physical 16-byte chunk of logical chunk c in LDS row r (a permutation of the
-// low 3 bits): 8 consecutive rows, or 4 consecutive rows x 2 adjacent chunks,
-// land on 8 different chunk slots, i.e. disjoint LDS banks.
+// Physical 16-byte chunk of logical chunk c in LDS row r.  LDS has 64 banks
+// of 4 bytes, i.e. 256-byte lines of 16 chunk slots.  The permutation makes
+//  * the K fragment read (16 lanes per cycle, 16 consecutive rows, one chunk)
+//  * the V transpose read (32 lanes per cycle, 4 consecutive rows x 4
+//    adjacent chunks)
+// touch 16 different chunk slots of a line, i.e. all 64 banks once.
+// d = 128: one row per line, chunk c in 0..15, XOR with a bit-rotation of r.
+// d = 64: two rows per line (slot = 8*(r&1) + chunk), chunk c in 0..7.
+template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-    return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
+    if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// One K tile and one V tile, HBM -> LDS stage (K at stage_base, V after it).
+// Buffer resources span the head's rows (bytes = N*D*2); rows past the end are
+// out of range and land as zeros.  gofs: this lane's byte offset within the
+// tile for each of its LPW 1 KiB loads; tbase: the tile's byte offset.
+template <int LPW, int TILE>
+__device__ __forceinline__ void load_kv_tile(const uint16_t* Kh, const uint16_t* Vh, int bytes,
+                                             int tbase, const int* gofs,
+                                             uint16_t* stage_base, int wave) {
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int region = wave * LPW + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(stage_base + region * 512), 16,
+                                                 gofs[i], tbase, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(stage_base + TILE + region * 512),
+                                                 16, gofs[i], tbase, 0, 0);
+    }
 }
 
 template <int D, int QS, bool CAUSAL>
@@ -160,8 +174,6 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             if (qrow < N) x = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + kc * 16 + g * 8);
             x ^= qflip;
             qop[qs][kc] = __builtin_bit_cast(bf16x8, x);
-            // only MFMAs read Q: keep it in AGPRs, leaving VGPRs to the softmax
-            asm volatile("" : "+a"(qop[qs][kc]));
         }
     }
 
@@ -183,38 +195,50 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // ---- HBM -> LDS, one tile: each wave issues LPW 1 KiB loads per tensor;
     //      lane l of a load writes LDS bytes 16l..16l+15 of its 1 KiB region,
     //      i.e. (row, physical chunk) = (region*RPK + l/CPR, l%CPR), and fetches
-    //      the logical chunk that belongs there.  Rows past N re-read row N-1
-    //      (finite data; those keys are masked and their V rows get p = 0).
-    auto load_tile = [&](int kt, uint16_t* ks, uint16_t* vs) __attribute__((always_inline)) {
+    //      the logical chunk that belongs there.  The loads go through buffer
+    //      resources spanning this head's N rows: rows past N are out of range
+    //      and land as zeros (those keys are masked, their V rows get p = 0).
+    int gofs[LPW];                             // byte offset within the tile
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int region = wave * LPW + i;
-            const int row = region * RPK + lane / CPR;
-            const int cl = swz(row, lane % CPR);
-            const int grow = min(kt * BN + row, N - 1);
-            const size_t goff = (size_t)grow * D + cl * 8;
-            __builtin_amdgcn_global_load_lds(Kh + goff, (lds_void*)(ks + region * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(Vh + goff, (lds_void*)(vs + region * 512), 16, 0, 0);
-        }
+    for (int i = 0; i < LPW; ++i) {
+        const int row = (wave * LPW + i) * RPK + lane / CPR;
+        gofs[i] = (row * D + swz<D>(row, lane % CPR) * 8) * 2;
+    }
+    auto load_tile = [&](int kt, uint16_t* stage_base) __device__ __attribute__((always_inline)) {
+        load_kv_tile<LPW, TILE>(Kh, Vh, N * D * 2, kt * BN * D * 2, &gofs[0], stage_base, wave);
     };
 
-    // ---- tile loop: double-buffered LDS, one barrier per tile.  Each step
-    //      waits for its own tile's loads, syncs (all loads landed, everyone is
-    //      done with the other buffer), starts the next tile's loads into the
-    //      other buffer, then computes on this one.
-    load_tile(0, smem, smem + TILE);
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const uint16_t* ks = smem + (kt & 1) * (2 * TILE);
-        const uint16_t* vs = ks + TILE;
+    // ---- per-lane LDS offsets (elements) of the MFMA operand reads; the
+    //      row offsets 32kb (+16cc, +8) do not change the swizzle, so they and
+    //      the stage offset are immediates.
+    int kofs[NKC];                             // K fragment, key row l32, chunk 2kc+g
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) kofs[kc] = l32 * D + swz<D>(l32, 2 * kc + g) * 8;
+    const int h = lane >> 4;
+    const int li = lane & 15;
+    int vofs[2][ND];                           // V transpose read, key row 4g+li/4 (+8)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            const int row = 4 * (h >> 1) + (li >> 2) + 8 * hl;
+            const int col = db * 32 + 16 * (h & 1) + 4 * (li & 3);
+            vofs[hl][db] = row * D + swz<D>(row, col >> 3) * 8 + (col & 7);
+        }
+
+    // ---- one key tile: wait for its loads, sync (all loads landed, everyone
+    //      is done with the other buffer), start the next tile's loads into the
+    //      other buffer, then scores, online softmax and PV on this one.
+    auto tile_step = [&](int kt, uint16_t* cur, uint16_t* nxt, auto mask_tag) __device__
+        __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const uint16_t* ks = cur;
+        const uint16_t* vs = cur + TILE;
         __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads have landed
         __syncthreads();
-        if (kt + 1 < n_kt) {
-            uint16_t* nk = smem + ((kt + 1) & 1) * (2 * TILE);
-            load_tile(kt + 1, nk, nk + TILE);
-        }
+        if (kt + 1 < n_kt) load_tile(kt + 1, nxt);
         const int k0 = kt * BN;
-        if (CAUSAL && k0 > wq0 + 32 * QS - 1) continue;   // tile above all of this wave's rows
-        const bool need_mask = kt >= n_full;
+        if (MASK && CAUSAL && k0 > wq0 + 32 * QS - 1) return;   // tile above all of this wave's rows
 
         // ---- S^T = K Q^T for 2 blocks of 32 keys; each K fragment feeds QS MFMAs
         f32x16 sacc[QS][2];
@@ -226,11 +250,10 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 for (int r = 0; r < 16; ++r) sacc[qs][kb][r] = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int row = kb * 32 + l32;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
                 const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(ks + row * D + swz(row, 2 * kc + g) * 8));
+                    bf16x8, *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + kofs[kc]));
 #pragma unroll
                 for (int qs = 0; qs < QS; ++qs)
                     sacc[qs][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[qs][kc],
@@ -238,33 +261,26 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
         }
 
-#pragma unroll
-        for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(sacc[qs][kb]));   // VALU reads these
-
         // ---- online softmax per query sub-block; lane holds query
         //      wq0 + 32qs + l32 and keys k0 + 32kb + 8(r/4) + 4g + r%4
         bf16x8 pop[QS][2][2];
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) {
             const int qrow = wq0 + 32 * qs + l32;
-            if (need_mask) {                   // ragged end of N or causal diagonal
+            if constexpr (MASK) {              // ragged end of N or causal diagonal:
+                // hide key k0 + 4g + off(kb, r) when it exceeds this row's last key
+                const int lim = (CAUSAL ? min(N - 1, qrow) : N - 1) - (k0 + 4 * g);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (key >= N || (CAUSAL && key > qrow)) sacc[qs][kb][r] = kNegInf;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[qs][kb][r] = kNegInf;
             }
             float mt = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    mt = fmaxf(mt, sacc[qs][kb][r]);
-                }
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[qs][kb][r]);
             mt = pair_max(mt);
             if (__any(mt > m_run[qs] + tau_raw)) {
                 const float m_new = fmaxf(m_run[qs], mt);
@@ -280,7 +296,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(sacc[qs][kb][r], c, -mc));
+                    const float p = fast_exp2(fmaf(sacc[qs][kb][r], c, -mc));
                     if (r & 1) ps1 += p; else ps0 += p;
                     pop[qs][kb][r >> 3][r & 7] = (__bf16)p;
                 }
@@ -289,24 +305,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
         // ---- O^T += V^T P^T; each V^T fragment feeds QS MFMAs.  Fragment for
         //      d rows db*32 .. +32 and keys 32kb + 16cc + {4g..4g+3, 8+4g..8+4g+3}:
-        //      two transpose loads, lane (16-lane group h, index i) addressing
-        //      key row 32kb + 16cc + 4g + i/4 (+8), columns d0 + 4(i%4).
-        const int h = lane >> 4;
-        const int li = lane & 15;
+        //      two transpose loads, lane (16-lane group h, index li) addressing
+        //      key row 32kb + 16cc + 4g + li/4 (+8), columns db*32 + 16(h&1) + 4(li&3).
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                const int r_lo = kb * 32 + cc * 16 + 4 * (h >> 1) + (li >> 2);
-                const int r_hi = r_lo + 8;
+                const uint16_t* vb = vs + (kb * 32 + cc * 16) * D;
 #pragma unroll
                 for (int db = 0; db < ND; ++db) {
-                    const int col = db * 32 + 16 * (h & 1) + 4 * (li & 3);
-                    const int ch = col >> 3;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(vs + r_lo * D + swz(r_lo, ch) * 8 + (col & 7)));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(vs + r_hi * D + swz(r_hi, ch) * 8 + (col & 7)));
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vofs[0][db]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vofs[1][db]));
                     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
                     const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
                     const u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -318,6 +327,25 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 }
             }
     };
+
+    // ---- tile loops: unmasked tiles unrolled by two (each body's LDS stage is
+    //      an immediate), then the few masked tiles (ragged end, causal diagonal)
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+    uint16_t* const stage0 = smem;
+    uint16_t* const stage1 = smem + 2 * TILE;
+    load_tile(0, stage0);
+    int kt = 0;
+    for (; kt < n_full; kt += 2) {
+        tile_step(kt, stage0, stage1, NoMask{});
+        if (kt + 1 < n_full) tile_step(kt + 1, stage1, stage0, NoMask{});
+    }
+    kt = n_full;
+    for (; kt < n_kt; ++kt) {
+        uint16_t* cur = (kt & 1) ? stage1 : stage0;
+        uint16_t* nxt = (kt & 1) ? stage0 : stage1;
+        tile_step(kt, cur, nxt, Mask{});
+    }
 
     // ---- epilogue: O = O_acc / l (bf16, round to nearest even), LSE = ln l + m
 #pragma unroll
