@@ -53,6 +53,22 @@ def decode_bytes(layout):
     return kv + small, logical + small
 
 
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch (read + written) from the committed counter summary
+    profiles/traffic.json, or None when the kernel source changed since."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)["kernels"][kernel_key]
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    except (OSError, KeyError, ValueError):
+        return None
+    if sha != rec["sha256_16"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def cpu_baseline(budget_s: float = 15.0):
     """The fp64 oracle, as it stands, on a bounded sample of the forward
     workload: whole (b, h) heads of the non-causal B=8 H=16 N=2048 d=128
@@ -93,6 +109,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
                     help="forward only (for profiling the forward kernel alone)")
+    ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode"],
+                    help="run one call per step (for per-kernel counter runs)")
+    ap.add_argument("--probe-copy", type=int, metavar="MIB",
+                    help="instead of the hot path, copy a buffer of MIB MiB a few times "
+                         "(a plain copy kernel of known size, to calibrate byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are "
@@ -105,6 +126,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.probe_copy:
+        n = args.probe_copy * 2 ** 20 // 4
+        src = torch.arange(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe_copy_bytes_each_way": n * 4, "copies": max(1, args.steps)}))
+        return
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
 
     # ---- forward inputs ----
@@ -119,7 +149,7 @@ def main():
     log("forward inputs ready")
 
     # ---- decode inputs ----
-    decode = not args.skip_decode
+    decode = not args.skip_decode and args.only in (None, "decode")
     if decode:
         L = w.decode_layout(**w.DECODE_C4)
         qdec = torch.from_numpy(w.decode_q(L)).to(dev).to(torch.bfloat16)
@@ -146,13 +176,19 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
+    run_nc = args.only in (None, "fwd-noncausal")
+    run_c = args.only in (None, "fwd-causal")
+    run_dec = decode and args.only in (None, "decode")
+
     def step(timed, acc):
         ev[0].record(stream)
-        fa.fa_fwd(qd, kd, vd, o_nc, lse_nc, False, cfg.scale)
+        if run_nc:
+            fa.fa_fwd(qd, kd, vd, o_nc, lse_nc, False, cfg.scale)
         ev[1].record(stream)
-        fa.fa_fwd(qd, kd, vd, o_c, lse_c, True, cfg.scale)
+        if run_c:
+            fa.fa_fwd(qd, kd, vd, o_c, lse_c, True, cfg.scale)
         ev[2].record(stream)
-        if decode:
+        if run_dec:
             fa.fa_paged_decode(qdec, kc, vc, bt, sl, o_dec, lse_dec, L.scale, ws)
         ev[3].record(stream)
         if timed:
@@ -212,8 +248,9 @@ def main():
                 "causal_frac_peak": round(tflops_c / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops_nc, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops_nc / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_kernel<bf16,128,non-causal>",
+                     "frac": round(tflops_nc / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("fwd_bf16_kernel<128,1,false> B=8 H=16 N=2048"),
+                     "kernel": "fwd_bf16_kernel<128,1,false>",
                      "flops_per_launch": f_nc},
     }
     if decode:
@@ -224,7 +261,12 @@ def main():
                          "logical_gbs": round(dec_logical / (t_dec * 1e-3) / 1e9, 1)}
         out["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs, 1),
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                  "traffic": measured_traffic("decode_partial_kernel<128> C4")}
+    if args.only is not None:
+        print(json.dumps({"only": args.only, "ms": {"fwd-noncausal": t_nc, "fwd-causal": t_c,
+                                                    "decode": t_dec}[args.only]}), flush=True)
+        return
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline()

@@ -91,8 +91,8 @@ typedef enum {
  *   stream    hipStream_t, or NULL
  *
  * Returns FA_OK, FA_ERR_INVALID (null q/k/v/o, B/H/N < 1, causal not 0/1,
- * non-finite scale, B*H*N*d beyond 2^62), FA_ERR_UNSUPPORTED (d not 64/128,
- * unknown dtype), or FA_ERR_HIP.
+ * non-finite scale, N*d*2 bytes of one head beyond 2^31, or more than 2^31-1
+ * work groups), FA_ERR_UNSUPPORTED (d not 64/128, unknown dtype), or FA_ERR_HIP.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, int causal, float scale,
@@ -127,7 +127,7 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int page_size,
  *   seq_lens     [S] int32, tokens cached per sequence       (read)
  *   o            [S][H][d] elements of `dtype`              (written)
  *   lse          [S][H] float32 natural-log log-sum-exp, or NULL
- *   num_seqs (S), H >= 1;  d: 128 (else FA_ERR_UNSUPPORTED);
+ *   num_seqs (S), H >= 1 (each at most 65535);  d: 64 or 128 (else FA_ERR_UNSUPPORTED);
  *   page_size: 16 (else FA_ERR_UNSUPPORTED);  max_blocks_per_seq >= 1;
  *   num_blocks >= 1;  scale finite;  dtype: FA_BF16 (FA_F32 -> UNSUPPORTED)
  *   workspace    device scratch of at least
