@@ -45,7 +45,8 @@ int main() {
     EXPECT_EQ(check_fwd(p, p, p, p, 65535, 65535, 2147483647, 128, 0, 1.f, FA_BF16),
               FA_ERR_INVALID);
     // forward: unsupported
-    EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1 << 22, 128, 0, 1.f, FA_BF16), FA_ERR_INVALID);
+    EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1 << 23, 128, 0, 1.f, FA_BF16), FA_ERR_INVALID);
+    EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, (1 << 23) - 1, 128, 0, 1.f, FA_BF16), FA_OK);
     EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1, 96, 0, 1.f, FA_BF16), FA_ERR_UNSUPPORTED);
     EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1, 256, 0, 1.f, FA_BF16), FA_ERR_UNSUPPORTED);
     EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1, 64, 0, 1.f, 7), FA_ERR_UNSUPPORTED);
