@@ -32,7 +32,7 @@ inline fa_status check_fwd(const void* q, const void* k, const void* v, const vo
     const double elems = double(B) * double(H) * double(N) * double(d);
     if (elems >= 4611686018427387904.0) return FA_ERR_INVALID;           // 2^62
     // one head's K or V is addressed with 32-bit byte offsets
-    if (double(N) * double(d) * 2.0 >= 2147483648.0) return FA_ERR_INVALID;
+    if ((double(N) + 64.0) * double(d) * 2.0 >= 2147483648.0) return FA_ERR_INVALID;
     // one work group per (b, h, block of query rows): the 1-D grid must fit
     const double groups = double(B) * double(H) * std::ceil(double(N) / kFwdBlockM);
     if (groups > 2147483647.0) return FA_ERR_INVALID;

@@ -46,7 +46,8 @@ int main() {
               FA_ERR_INVALID);
     // forward: unsupported
     EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1 << 23, 128, 0, 1.f, FA_BF16), FA_ERR_INVALID);
-    EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, (1 << 23) - 1, 128, 0, 1.f, FA_BF16), FA_OK);
+    EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, (1 << 23) - 64, 128, 0, 1.f, FA_BF16), FA_ERR_INVALID);
+    EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, (1 << 23) - 65, 128, 0, 1.f, FA_BF16), FA_OK);
     EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1, 96, 0, 1.f, FA_BF16), FA_ERR_UNSUPPORTED);
     EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1, 256, 0, 1.f, FA_BF16), FA_ERR_UNSUPPORTED);
     EXPECT_EQ(check_fwd(p, p, p, p, 1, 1, 1, 64, 0, 1.f, 7), FA_ERR_UNSUPPORTED);
