@@ -11,8 +11,11 @@
 // O ("FlashAttention-2 GPU work partitioning", iPLEX blog, section 3).
 //
 // gfx950 design
-//  * Work group = 4 waves; each wave owns QS x 32 query rows (QS = 2 at d=128),
-//    so every K/V fragment read from LDS feeds QS matrix instructions.
+//  * Work group = 4 waves; each wave owns QS x 32 query rows, and every K/V
+//    fragment read from LDS feeds QS matrix instructions.  QS = 1 is what runs:
+//    all of a wave's state then fits in 256 VGPRs and two work groups share a
+//    CU, so one wave's softmax overlaps the other's MFMAs (QS = 2 halves the
+//    LDS reads per flop but needs one wave per SIMD, measured slower).
 //  * K and V tiles (64 keys) go HBM -> LDS with global_load_lds_dwordx4 (no
 //    register staging), double-buffered: the next tile is in flight while the
 //    current one is computed, with one barrier per tile.  Rows are stored with
@@ -55,12 +58,6 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
-#ifndef FA_QS128
-#define FA_QS128 1
-#endif
-#ifndef FA_QS64
-#define FA_QS64 1
-#endif
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -260,6 +257,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                                                                            sacc[qs][kb], 0, 0, 0);
             }
         }
+        {
+            // schedule: keep four K fragment reads (DS read, 0x100) in flight
+            // ahead of the score MFMAs (0x008)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * NKC * QS - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
 
         // ---- online softmax per query sub-block; lane holds query
         //      wq0 + 32qs + l32 and keys k0 + 32kb + 8(r/4) + 4g + r%4
@@ -396,10 +404,10 @@ hipError_t fa_launch_fwd_bf16(const void* q, const void* k, const void* v, void*
                               int B, int H, int N, int d, int causal, float scale,
                               hipStream_t stream) {
     if (d == 128)
-        return causal ? launch<128, FA_QS128, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                      : launch<128, FA_QS128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+        return causal ? launch<128, 1, true>(q, k, v, o, lse, B, H, N, scale, stream)
+                      : launch<128, 1, false>(q, k, v, o, lse, B, H, N, scale, stream);
     if (d == 64)
-        return causal ? launch<64, FA_QS64, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                      : launch<64, FA_QS64, false>(q, k, v, o, lse, B, H, N, scale, stream);
+        return causal ? launch<64, 1, true>(q, k, v, o, lse, B, H, N, scale, stream)
+                      : launch<64, 1, false>(q, k, v, o, lse, B, H, N, scale, stream);
     return hipErrorInvalidValue;
 }
