@@ -39,7 +39,8 @@ import math
 
 import numpy as np
 
-__all__ = ["attention_fp64", "attention_bruteforce", "paged_gather_fp64", "paged_decode_fp64"]
+__all__ = ["attention_fp64", "attention_bruteforce", "paged_gather_fp64", "paged_decode_fp64",
+           "attention_backward_fp64"]
 
 
 def _as64(x) -> np.ndarray:
@@ -167,3 +168,46 @@ def paged_decode_fp64(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     if pairs is None:
         return o.reshape(S, H, d), lse.reshape(S, H)
     return o, lse
+
+
+def attention_backward_fp64(q, k, v, do, *, causal: bool = False, scale: float | None = None):
+    """Gradients of O = softmax(scale * Q K^T) V with respect to Q, K, V, float64.
+
+    Written from the chain rule of the definition above, with the softmax
+    probabilities materialised per (batch, head):
+        P = softmax(S) row-wise (hidden keys get P = 0),
+        dV = P^T dO,
+        dP = dO V^T,
+        dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)       (softmax Jacobian),
+        dQ = scale * dS K,   dK = scale * dS^T Q.
+    The backward pass the pages describe reuses the forward's stored row
+    statistics and recomputes the scores blockwise ("PagedAttention vs
+    FlashAttention: key differences", training section; "LLM study notes",
+    FlashAttention core principles: recomputation); the result it must reach is
+    this plain gradient.  Note sum_k P_ik dP_ik = sum_d dO_id O_id.
+
+    q, k, v, do: ``[..., N, d]``.  Returns ``(dq, dk, dv)`` as float64.
+    """
+    q, k, v, do = (_as64(x) for x in (q, k, v, do))
+    *lead, n, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    g = int(np.prod(lead)) if lead else 1
+    qf, kf, vf, dof = (x.reshape(g, n, d) for x in (q, k, v, do))
+    dq = np.empty_like(qf)
+    dk = np.empty_like(kf)
+    dv = np.empty_like(vf)
+    for gi in range(g):
+        s_ = scale * (qf[gi] @ kf[gi].T)
+        if causal:
+            s_ = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s_)
+        m = s_.max(axis=1, keepdims=True)
+        p_ = np.exp(s_ - m)
+        p_ /= p_.sum(axis=1, keepdims=True)
+        dv[gi] = p_.T @ dof[gi]
+        dp = dof[gi] @ vf[gi].T
+        ds = p_ * (dp - (p_ * dp).sum(axis=1, keepdims=True))
+        dq[gi] = scale * (ds @ kf[gi])
+        dk[gi] = scale * (ds.T @ qf[gi])
+    shape = tuple(lead) + (n, d)
+    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
