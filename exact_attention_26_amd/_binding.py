@@ -42,6 +42,12 @@ def load_library():
     lib.fa_fwd.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                            c.c_int, c.c_int, c.c_int, c.c_int, c.c_int, c.c_float,
                            c.c_int, c.c_void_p]
+    lib.fa_bwd_workspace_size.restype = c.c_size_t
+    lib.fa_bwd_workspace_size.argtypes = [c.c_int] * 4
+    lib.fa_bwd.restype = c.c_int
+    lib.fa_bwd.argtypes = [c.c_void_p] * 9 + [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int,
+                                              c.c_float, c.c_int, c.c_void_p, c.c_size_t,
+                                              c.c_void_p]
     lib.fa_paged_decode_workspace_size.restype = c.c_size_t
     lib.fa_paged_decode_workspace_size.argtypes = [c.c_int] * 5
     lib.fa_paged_decode.restype = c.c_int
@@ -72,6 +78,10 @@ def fa_status_string(status: int) -> str:
 
 def fa_last_hip_error() -> int:
     return int(load_library().fa_last_hip_error())
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H, N, d))
 
 
 def fa_paged_decode_workspace_size(num_seqs: int, H: int, d: int, page_size: int,
@@ -134,6 +144,31 @@ def fa_fwd(q, k, v, o, lse, causal: bool, scale: float) -> None:
         raise FaError(st, "fa_fwd")
 
 
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace) -> None:
+    """Call ``fa_bwd`` on ``[B][H][N][d]`` tensors; ``lse`` float32 [B][H][N];
+    ``workspace`` a uint8 device tensor of at least ``fa_bwd_workspace_size`` bytes."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][H][N][d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_dense(name, t, dev)
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q's shape and dtype")
+    _check_dense("lse", lse, dev)
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != _torch().float32:
+        raise ValueError("lse must be float32 [B][H][N]")
+    _check_dense("workspace", workspace, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
+                               float(scale), _dtype_code(q), _ptr(workspace), ws_bytes,
+                               _stream(dev))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+
+
 def fa_paged_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale: float,
                     workspace) -> None:
     """Call ``fa_paged_decode``.  ``q``/``o``: [S][H][d]; caches
@@ -181,6 +216,22 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None):
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, causal, scale)
     return o, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                       workspace=None):
+    """Exact attention backward from the forward's ``(o, lse)``.  Returns ``(dq, dk, dv)``;
+    allocates the workspace if not given.  scale defaults to 1/sqrt(d)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_size(B, H, N, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace)
+    return dq, dk, dv
 
 
 def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None,

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["fa_fwd.hip", "fa_fwd_bf16.hip", "fa_decode.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_fwd_bf16.hip", "fa_bwd.hip", "fa_decode.hip", "fa_api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + INCLUDE, "-I" + CSRC]

@@ -28,6 +28,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                                     static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+    return fa_host::bwd_workspace_bytes(B, H, N, d);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    const fa_status st = fa_host::check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal,
+                                            scale, dtype, workspace, workspace_bytes);
+    if (st != FA_OK) return st;
+    return hip_status(fa_launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal,
+                                         scale, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int page_size,
                                       int max_blocks_per_seq) {
     return fa_host::decode_workspace_bytes(num_seqs, H, d, page_size, max_blocks_per_seq);

@@ -14,6 +14,13 @@ hipError_t fa_launch_fwd_bf16(const void* q, const void* k, const void* v, void*
                               int B, int H, int N, int d, int causal, float scale,
                               hipStream_t stream);
 
+// bf16 backward (fa_bwd.hip): row statistics, dK/dV, dQ; workspace holds the
+// row statistics (fa_host::bwd_workspace_bytes)
+hipError_t fa_launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int B, int H, int N, int d, int causal, float scale, void* workspace,
+                              hipStream_t stream);
+
 hipError_t fa_launch_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   void* o, float* lse, int S, int H, int d,

@@ -41,6 +41,40 @@ inline fa_status check_fwd(const void* q, const void* k, const void* v, const vo
     return FA_OK;
 }
 
+// Backward: rows per tile of the row statistics; each tile keeps 256 floats
+// (1 KiB, one LDS DMA load): lse*log2(e) of its 64 rows, their dO.O, 128 unused.
+constexpr int kBwdStatsRows = 64;
+constexpr int kBwdStatsTileBytes = 1024;
+
+inline bool bwd_head_dim_supported(int d) { return d == 64 || d == 128; }
+
+// Backward workspace bytes for these sizes (0 = invalid sizes).
+inline size_t bwd_workspace_bytes(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    const double tiles = double(B) * H * std::ceil(double(N) / kBwdStatsRows);
+    if (tiles * kBwdStatsTileBytes > 1.0e15) return 0;
+    return size_t(B) * size_t(H) * size_t((N + kBwdStatsRows - 1) / kBwdStatsRows) *
+           size_t(kBwdStatsTileBytes);
+}
+
+inline fa_status check_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const void* lse, const void* dout, const void* dq, const void* dk,
+                           const void* dv, int B, int H, int N, int d, int causal, float scale,
+                           int dtype, const void* ws, size_t ws_bytes) {
+    if (!lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID;
+    // the forward's checks cover q, k, v, o, the sizes, the scale and the
+    // 32-bit offsets; its grid bound (one group per 128 rows) covers the
+    // backward's 128-row groups, and the statistics grid has 2x that many
+    const fa_status st = check_fwd(q, k, v, o, B, H, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    if (double(B) * H * std::ceil(double(N) / kBwdStatsRows) > 2147483647.0) return FA_ERR_INVALID;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!bwd_head_dim_supported(d)) return FA_ERR_UNSUPPORTED;
+    const size_t need = bwd_workspace_bytes(B, H, N, d);
+    if (need == 0 || !ws || ws_bytes < need) return FA_ERR_INVALID;
+    return FA_OK;
+}
+
 inline int decode_max_splits(int max_blocks_per_seq) {
     return (max_blocks_per_seq + kDecodeSplitPages - 1) / kDecodeSplitPages;
 }

@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "FwdConfig", "FWD_CONFIGS", "round_to_bf16", "fwd_inputs",
     "DecodeLayout", "decode_layout", "decode_q", "decode_pool", "decode_pool_pages",
-    "page_valid_slots", "fwd_config_inputs",
+    "page_valid_slots", "fwd_config_inputs", "bwd_dout",
     "DECODE_C4",
 ]
 
@@ -117,6 +117,24 @@ def fwd_inputs(B: int, H: int, N: int, d: int, *, seed: int, dtype: str = "bf16"
 def fwd_config_inputs(cfg: FwdConfig):
     return fwd_inputs(cfg.B, cfg.H, cfg.N, cfg.d, seed=cfg.seed, dtype=cfg.dtype,
                       sigma_qk=cfg.sigma_qk, sigma_v=cfg.sigma_v)
+
+
+def bwd_dout(B: int, H: int, N: int, d: int, *, seed: int, dtype: str = "bf16",
+             sigma: float = 1.0) -> np.ndarray:
+    """The incoming gradient dO of shape ``[B][H][N][d]`` for a backward pass.
+
+    Drawn from its own stream (``default_rng([seed, 5])``), so the forward
+    inputs of the same seed are unchanged; ``standard_normal * sigma``,
+    rounded once to bf16 for ``dtype="bf16"``.
+    """
+    x = np.random.default_rng([seed, 5]).standard_normal((B, H, N, d), dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return x
 
 
 # --------------------------------------------------------------------------

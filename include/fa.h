@@ -1,11 +1,13 @@
 /*
  * fa.h - C ABI of libfa.so: exact scaled-dot-product attention on MI355X (gfx950).
  *
- * Two operations sit behind this interface.
+ * Three operations sit behind this interface.
  *
  *   fa_fwd           the attention forward pass computed FlashAttention-style:
  *                    Q, K, V in device memory, O (and the per-row log-sum-exp)
  *                    written back, the N x N score matrix never stored.
+ *   fa_bwd           its backward pass: dQ, dK, dV from dO, recomputing the
+ *                    scores from Q, K and the stored log-sum-exp.
  *   fa_paged_decode  one query token per sequence attending to a KV cache that
  *                    is stored in fixed-size pages and reached through a block
  *                    table.
@@ -97,6 +99,54 @@ typedef enum {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, int causal, float scale,
                  int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_size - bytes of device workspace fa_bwd needs for these
+ * sizes (0 if the sizes are invalid).  Host-only, no HIP call.  It is
+ * B * H * ceil(N / 64) KiB: per 64 rows, their log-sum-exp and dO . O.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fa_bwd - attention backward pass: dQ, dK, dV from dO.
+ *
+ * The pages present the method as built for training, with a backward pass
+ * that keeps only the forward's output and row statistics and recomputes the
+ * attention scores block by block instead of storing the N x N matrix
+ * ("PagedAttention vs FlashAttention: key differences", training section;
+ * "LLM study notes", DEVOCEAN tech blog, FlashAttention core principles:
+ * recomputation; the row statistics are the lse output of fa_fwd).  With
+ * P = softmax(scale * Q K^T) (the same mask as the forward) it computes the
+ * plain gradient of O = P V:
+ *     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - rowsum(dO o O)),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q.
+ * No N x N matrix is stored and no atomics are used (deterministic).
+ *
+ *   q, k, v     [B][H][N][d] bf16, the forward's inputs          (read)
+ *   o           [B][H][N][d] bf16, the forward's output          (read)
+ *   lse         [B][H][N] float32, the forward's natural-log lse (read)
+ *   dout        [B][H][N][d] bf16, gradient of the loss w.r.t. o (read)
+ *   dq, dk, dv  [B][H][N][d] bf16 gradients                      (written;
+ *               must not alias any input or each other)
+ *   B, H, N, d, causal, scale   as in fa_fwd (and equal to the forward's)
+ *   dtype       FA_BF16 (FA_F32 -> FA_ERR_UNSUPPORTED)
+ *   workspace   device scratch of at least fa_bwd_workspace_size(B, H, N, d)
+ *               bytes, owned by the caller; contents on entry do not matter;
+ *               it must not be shared with a call still running on another
+ *               stream.
+ *   stream      hipStream_t, or NULL
+ *
+ * o and lse are taken as given: with another o or lse the result is the
+ * gradient formula above evaluated with them, not the true gradient.
+ *
+ * Returns FA_OK, FA_ERR_INVALID (any null pointer, the size checks of fa_fwd,
+ * workspace NULL or too small), FA_ERR_UNSUPPORTED (d not 64/128, dtype not
+ * FA_BF16), or FA_ERR_HIP.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, int causal, float scale,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fa_paged_decode_workspace_size - bytes of device workspace fa_paged_decode

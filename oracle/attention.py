@@ -170,7 +170,8 @@ def paged_decode_fp64(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     return o, lse
 
 
-def attention_backward_fp64(q, k, v, do, *, causal: bool = False, scale: float | None = None):
+def attention_backward_fp64(q, k, v, do, *, causal: bool = False, scale: float | None = None,
+                            row_block: int | None = None):
     """Gradients of O = softmax(scale * Q K^T) V with respect to Q, K, V, float64.
 
     Written from the chain rule of the definition above, with the softmax
@@ -186,28 +187,36 @@ def attention_backward_fp64(q, k, v, do, *, causal: bool = False, scale: float |
     FlashAttention core principles: recomputation); the result it must reach is
     this plain gradient.  Note sum_k P_ik dP_ik = sum_d dO_id O_id.
 
+    ``row_block`` (default: all rows at once) takes the query rows in blocks
+    of that many, which only bounds memory: each row's P, dP, dS and dQ are
+    computed exactly as above, and dK, dV add up the blocks' contributions.
+
     q, k, v, do: ``[..., N, d]``.  Returns ``(dq, dk, dv)`` as float64.
     """
     q, k, v, do = (_as64(x) for x in (q, k, v, do))
     *lead, n, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    rb = n if row_block is None else max(1, int(row_block))
     g = int(np.prod(lead)) if lead else 1
     qf, kf, vf, dof = (x.reshape(g, n, d) for x in (q, k, v, do))
     dq = np.empty_like(qf)
-    dk = np.empty_like(kf)
-    dv = np.empty_like(vf)
+    dk = np.zeros_like(kf)
+    dv = np.zeros_like(vf)
+    keys = np.arange(n)
     for gi in range(g):
-        s_ = scale * (qf[gi] @ kf[gi].T)
-        if causal:
-            s_ = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s_)
-        m = s_.max(axis=1, keepdims=True)
-        p_ = np.exp(s_ - m)
-        p_ /= p_.sum(axis=1, keepdims=True)
-        dv[gi] = p_.T @ dof[gi]
-        dp = dof[gi] @ vf[gi].T
-        ds = p_ * (dp - (p_ * dp).sum(axis=1, keepdims=True))
-        dq[gi] = scale * (ds @ kf[gi])
-        dk[gi] = scale * (ds.T @ qf[gi])
+        for r0 in range(0, n, rb):
+            rows = np.arange(r0, min(n, r0 + rb))
+            s_ = scale * (qf[gi, rows] @ kf[gi].T)
+            if causal:
+                s_ = np.where(keys[None, :] > rows[:, None], -np.inf, s_)
+            m = s_.max(axis=1, keepdims=True)
+            p_ = np.exp(s_ - m)
+            p_ /= p_.sum(axis=1, keepdims=True)
+            dv[gi] += p_.T @ dof[gi, rows]
+            dp = dof[gi, rows] @ vf[gi].T
+            ds = p_ * (dp - (p_ * dp).sum(axis=1, keepdims=True))
+            dq[gi, rows] = scale * (ds @ kf[gi])
+            dk[gi] += scale * (ds.T @ qf[gi, rows])
     shape = tuple(lead) + (n, d)
     return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)

@@ -86,6 +86,37 @@ int main() {
     EXPECT_EQ(check_decode(p, p, p, p, p, p, 64, 32, 128, 16, 512, 17874, 0.1f, FA_F32, p, ws),
               FA_ERR_UNSUPPORTED);
 
+    // backward workspace: one KiB per 64 rows of every head
+    EXPECT_EQ(bwd_workspace_bytes(8, 16, 2048, 128), 8ull * 16 * 32 * 1024);
+    EXPECT_EQ(bwd_workspace_bytes(1, 1, 65, 64), 2ull * 1024);
+    EXPECT_EQ(bwd_workspace_bytes(1, 1, 0, 64), 0);
+    const size_t bws = bwd_workspace_bytes(8, 16, 2048, 128);
+    // backward: valid
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 8, 16, 2048, 128, 1, 0.088f, FA_BF16, p, bws),
+              FA_OK);
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 1, 64, 0, -0.5f, FA_BF16, p, 1024),
+              FA_OK);
+    // backward: invalid
+    EXPECT_EQ(check_bwd(p, p, p, p, nullptr, p, p, p, p, 1, 1, 1, 64, 0, 1.f, FA_BF16, p, 1024),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_bwd(p, p, p, p, p, nullptr, p, p, p, 1, 1, 1, 64, 0, 1.f, FA_BF16, p, 1024),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, nullptr, 1, 1, 1, 64, 0, 1.f, FA_BF16, p, 1024),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_bwd(nullptr, p, p, p, p, p, p, p, p, 1, 1, 1, 64, 0, 1.f, FA_BF16, p, 1024),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 8, 16, 2048, 128, 1, 0.088f, FA_BF16, p,
+                        bws - 1), FA_ERR_INVALID);
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 1, 64, 0, 1.f, FA_BF16, nullptr, 1024),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 1, 64, 0, nan, FA_BF16, p, 1024),
+              FA_ERR_INVALID);
+    // backward: unsupported
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 1, 64, 0, 1.f, FA_F32, p, 1024),
+              FA_ERR_UNSUPPORTED);
+    EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 1, 96, 0, 1.f, FA_BF16, p, 1024),
+              FA_ERR_UNSUPPORTED);
+
     EXPECT_EQ(std::string_view(status_string(FA_OK)).size() > 0, 1);
     if (failures) {
         std::fprintf(stderr, "%d check(s) failed\n", failures);

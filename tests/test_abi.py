@@ -23,8 +23,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted([
-        "fa_fwd", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_status_string",
-        "fa_last_hip_error"])
+        "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
+        "fa_paged_decode_workspace_size", "fa_status_string", "fa_last_hip_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -64,6 +64,34 @@ def _fwd(**kw):
 ])
 def test_fwd_rejects_before_launch(kw, status):
     assert _fwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    # one KiB per 64 rows of every head
+    assert fa.fa_bwd_workspace_size(8, 16, 2048, 128) == 8 * 16 * 32 * 1024
+    assert fa.fa_bwd_workspace_size(1, 2, 65, 64) == 2 * 2 * 1024
+    assert fa.fa_bwd_workspace_size(1, 1, 0, 64) == 0
+
+
+def _bwd(**kw):
+    ws = fa.fa_bwd_workspace_size(1, 1, 16, 64)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1,
+             H=1, N=16, d=64, causal=0, scale=0.125, dtype=fa.FA_BF16, ws=FAKE, wsb=ws)
+    a.update(kw)
+    return fa.load_library().fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                    a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                                    a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=None), 1), (dict(B=0), 1), (dict(N=0), 1), (dict(causal=2), 1),
+    (dict(scale=float("inf")), 1), (dict(ws=None), 1), (dict(wsb=1023), 1),
+    (dict(d=96), 2), (dict(dtype=fa.FA_F32), 2), (dict(dtype=7), 2),
+])
+def test_bwd_rejects_before_launch(kw, status):
+    assert _bwd(**kw) == status
 
 
 def test_decode_workspace_size():

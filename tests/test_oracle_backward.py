@@ -127,3 +127,18 @@ def test_backward_mutant_is_caught(kind):
 def test_backward_unmutated_copy_passes():
     for pin in BWD_PINS:
         pin(_mutant("none"))
+
+
+def test_backward_row_blocks_bound_memory_only():
+    # the row-blocked form (used at N = 16384) is the same gradient: every
+    # pin above, and agreement with the unblocked form on ragged blocks
+    for pin in BWD_PINS:
+        pin(lambda *a, **kw: attention_backward_fp64(*a, row_block=4, **kw))
+    rng = np.random.default_rng(34)
+    q, k, v, do = (rng.standard_normal((2, 37, 8)) for _ in range(4))
+    for causal in (False, True):
+        full = attention_backward_fp64(q, k, v, do, causal=causal, scale=0.4)
+        for rb in (1, 5, 16, 36):
+            part = attention_backward_fp64(q, k, v, do, causal=causal, scale=0.4, row_block=rb)
+            for a, b in zip(full, part):
+                np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
