@@ -11,8 +11,10 @@ One step = the whole hot path over one batch of synthetic input, resident in HBM
 forward calls over their kernel time, HIP events on the launch stream).  The
 decode's HBM GB/s, per-call figures, the roofline of the dominant kernel and
 the CPU oracle's rate on a bounded sample are reported in the same JSON line.
+The backward pass (fa_bwd) of both forward calls is timed after the steps, in
+a loop of its own, and reported under "bwd" (it is not part of the step).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--skip-bwd]
 """
 from __future__ import annotations
 
@@ -37,6 +39,13 @@ def fwd_flops(B, H, N, d, causal):
     """Algorithmic FLOPs: 4*N^2*d per head (2 for QK^T, 2 for PV); causal counts
     only the N(N+1)/2 visible pairs.  Masked work and exponentials not counted."""
     return 2.0 * B * H * d * N * (N + 1) if causal else 4.0 * B * H * N * N * d
+
+
+def bwd_flops(B, H, N, d, causal):
+    """Algorithmic backward FLOPs: the five N x N x d products of the gradient
+    (S recomputed, dP, dV, dQ, dK), 2.5x the forward's.  The dK/dV and dQ
+    kernels recompute S and dP once more each; that extra work is not counted."""
+    return 2.5 * fwd_flops(B, H, N, d, causal)
 
 
 def decode_bytes(layout):
@@ -109,7 +118,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
                     help="forward only (for profiling the forward kernel alone)")
-    ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode"],
+    ap.add_argument("--skip-bwd", action="store_true", help="do not time the backward pass")
+    ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode", "bwd-noncausal",
+                                       "bwd-causal"],
                     help="run one call per step (for per-kernel counter runs)")
     ap.add_argument("--probe-copy", type=int, metavar="MIB",
                     help="instead of the hot path, copy a buffer of MIB MiB a few times "
@@ -176,8 +187,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
-    run_nc = args.only in (None, "fwd-noncausal")
-    run_c = args.only in (None, "fwd-causal")
+    run_nc = args.only in (None, "fwd-noncausal", "bwd-noncausal")
+    run_c = args.only in (None, "fwd-causal", "bwd-causal")
     run_dec = decode and args.only in (None, "decode")
 
     def step(timed, acc):
@@ -263,9 +274,44 @@ def main():
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": round(gbs / PEAK_HBM_GBS, 4),
                                   "traffic": measured_traffic("decode_partial_kernel<128> C4")}
+    # ---- backward of both forward calls, its own timed loop ----
+    bwd_modes = [] if args.skip_bwd else [m for m in (False, True)
+                                          if args.only in (None, f"bwd-{'causal' if m else 'noncausal'}")]
+    t_bwd = {}
+    if bwd_modes:
+        do = torch.from_numpy(w.bwd_dout(cfg.B, cfg.H, cfg.N, cfg.d, seed=cfg.seed)).to(dev)
+        do = do.to(torch.bfloat16)
+        wsb = torch.empty(fa.fa_bwd_workspace_size(cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.uint8,
+                          device=dev)
+        dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+        fwd_out = {False: (o_nc, lse_nc), True: (o_c, lse_c)}
+        evb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for causal in bwd_modes:
+            o_, lse_ = fwd_out[causal]
+            for _ in range(args.warmup):
+                fa.fa_bwd(qd, kd, vd, o_, lse_, do, dq, dk, dv, causal, cfg.scale, wsb)
+            torch.cuda.synchronize()
+            tot = 0.0
+            for _ in range(args.steps):
+                evb[0].record(stream)
+                fa.fa_bwd(qd, kd, vd, o_, lse_, do, dq, dk, dv, causal, cfg.scale, wsb)
+                evb[1].record(stream)
+                evb[1].synchronize()
+                tot += evb[0].elapsed_time(evb[1])
+            t_bwd[causal] = tot / args.steps
+        log("backward timed")
+        out["bwd"] = {}
+        for causal in bwd_modes:
+            tag = "causal" if causal else "noncausal"
+            tf = bwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, causal) / (t_bwd[causal] * 1e-3) / 1e12
+            out["bwd"].update({f"{tag}_ms": round(t_bwd[causal], 4), f"{tag}_tflops": round(tf, 2),
+                               f"{tag}_frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        out["bwd"]["flops"] = "2.5x forward (10 N^2 d per head non-causal)"
+
     if args.only is not None:
-        print(json.dumps({"only": args.only, "ms": {"fwd-noncausal": t_nc, "fwd-causal": t_c,
-                                                    "decode": t_dec}[args.only]}), flush=True)
+        ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,
+              "bwd-noncausal": t_bwd.get(False), "bwd-causal": t_bwd.get(True)}[args.only]
+        print(json.dumps({"only": args.only, "ms": ms}), flush=True)
         return
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -104,7 +104,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     constexpr int NKC = D / 16;
     constexpr int ND = D / 32;
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+    // two stages as separate arrays, so that reads of one stage are known not
+    // to alias the asynchronous loads into the other (no wait for those loads)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem1[STAGE];
 
     // work group -> (b*h, key block), XCD-aware as in the forward; causal key
     // blocks come in increasing order, i.e. the longest (earliest keys) first
@@ -166,20 +169,39 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads have landed
         __syncthreads();
         if (qt + 1 < n_qt) load_tile(qt + 1, nxt);
+        // keep the dV / dK accumulators in AGPRs for the whole loop (an empty
+        // asm with an AGPR operand; it emits no instruction)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            asm volatile("" : "+a"(dvacc[db]));
+            asm volatile("" : "+a"(dkacc[db]));
+        }
         const int q0 = qt * BQ;
         if (MASK && CAUSAL && q0 + BQ - 1 < wk0) return;   // every query precedes every key
         const uint16_t* qs = cur;
         const uint16_t* dos = cur + TILE;
         const float* sts = reinterpret_cast<const float*>(cur + 2 * TILE);
 
-        // S = Q K^T and dP = dO V^T for two 32-query blocks
+        // The tile is worked as a two-stage software pipeline over its two
+        // 32-query blocks, so that one block's softmax (VALU) overlaps the
+        // other block's matrix products:
+        //   A: S, dP of block 0
+        //   B: S, dP of block 1         | P, dS of block 0
+        //   C: dV, dK from block 0      | P, dS of block 1
+        //   D: dV, dK from block 1
+        // Each phase ends in a scheduling fence; inside it the pattern keeps
+        // LDS operand reads a few MFMAs ahead and spreads the VALU work
+        // between the MFMAs.
+        using H0 = std::integral_constant<int, 0>;
+        using H1 = std::integral_constant<int, 1>;
         f32x16 sacc[2], pacc[2];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        bf16x8 pop[2][2], dsop[2][2];
+
+        // S = Q K^T and dP = dO V^T of one 32-query block (16 MFMAs)
+        auto scores = [&](auto hbt) __device__ __attribute__((always_inline)) {
+            constexpr int hb = decltype(hbt)::value;
 #pragma unroll
             for (int r = 0; r < 16; ++r) { sacc[hb][r] = 0.f; pacc[hb][r] = 0.f; }
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
                 const bf16x8 a = __builtin_bit_cast(
@@ -189,15 +211,15 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                     bf16x8, *reinterpret_cast<const u32x4*>(dos + hb * 32 * D + rofs[kc]));
                 pacc[hb] = mfma(b, vop[kc], pacc[hb]);
             }
+        };
 
-        // P and dS; lane holds key `key` and queries q0 + 32hb + 8i + 4g + j
-        // in register r = 4i + j.  Masked: keys after the query (causal) and
-        // queries past N.
+        // P and dS of one block; lane holds key `key` and queries
+        // q0 + 32hb + 8i + 4g + j in register r = 4i + j.  Masked: keys after
+        // the query (causal) and queries past N.
         const int lo = CAUSAL ? key - (q0 + 4 * g) : INT_MIN;
         const int hi = N - 1 - (q0 + 4 * g);
-        bf16x8 pop[2][2], dsop[2][2];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        auto softmax = [&](auto hbt) __device__ __attribute__((always_inline)) {
+            constexpr int hb = decltype(hbt)::value;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float4 l4 = *reinterpret_cast<const float4*>(sts + 32 * hb + 8 * i + 4 * g);
@@ -217,11 +239,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                     dsop[hb][r >> 3][r & 7] = (__bf16)ds;
                 }
             }
+        };
 
-        // dV^T += dO^T P and dK^T += Q^T dS over the tile's 4 chunks of 16
-        // queries; the query order inside a chunk matches the registers above
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        // dV^T += dO^T P and dK^T += Q^T dS over the block's two chunks of 16
+        // queries (16 MFMAs); the query order inside a chunk matches the
+        // registers of P and dS
+        auto grads = [&](auto hbt) __device__ __attribute__((always_inline)) {
+            constexpr int hb = decltype(hbt)::value;
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int rb = (32 * hb + 16 * cc) * D;
@@ -233,26 +257,79 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                     dkacc[db] = mfma(b, dsop[hb][cc], dkacc[db]);
                 }
             }
+        };
+
+        constexpr int NM = 2 * NKC;            // MFMAs per phase (= 4 ND)
+        // A
+        scores(H0{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NM - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // B
+        scores(H1{});
+        softmax(H0{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // C
+        grads(H0{});
+        softmax(H1{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // D
+        grads(H1{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 3);
+#pragma unroll
+        for (int i = 0; i < NM - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 3);
     };
 
     // query tiles: the two tiles that straddle the diagonal (causal), then the
     // unmasked ones, then the ragged last tile
     using NoMask = std::integral_constant<bool, false>;
     using Mask = std::integral_constant<bool, true>;
-    uint16_t* const stage0 = smem;
-    uint16_t* const stage1 = smem + STAGE;
+    uint16_t* const stage0 = smem0;
+    uint16_t* const stage1 = smem1;
     const int qt_begin = CAUSAL ? k0 / BQ : 0;
     const int qt_diag_end = CAUSAL ? min(n_qt, (k0 + BK) / BQ) : 0;
     const int n_full = N / BQ;
+    // tile qt lives in stage (qt - qt_begin) & 1 and every call names its
+    // stages statically.  The diagonal tiles (at most two) come first, so the
+    // unmasked pairs start on stage 0 (qt_diag_end - qt_begin is 0 or 2
+    // whenever an unmasked tile exists), and the rest (an odd last full tile,
+    // the ragged tile: at most two) start on stage 0 again.  The mask hides
+    // nothing in a full tile past the diagonal.
     load_tile(qt_begin, stage0);
-    int it = 0;
     int qt = qt_begin;
-    for (; qt < qt_diag_end; ++qt, ++it)
-        tile_step(qt, (it & 1) ? stage1 : stage0, (it & 1) ? stage0 : stage1, Mask{});
-    for (; qt < n_full; ++qt, ++it)
-        tile_step(qt, (it & 1) ? stage1 : stage0, (it & 1) ? stage0 : stage1, NoMask{});
-    for (; qt < n_qt; ++qt, ++it)
-        tile_step(qt, (it & 1) ? stage1 : stage0, (it & 1) ? stage0 : stage1, Mask{});
+    if (qt < qt_diag_end) tile_step(qt++, stage0, stage1, Mask{});
+    if (qt < qt_diag_end) tile_step(qt++, stage1, stage0, Mask{});
+    for (; qt + 1 < n_full; qt += 2) {
+        tile_step(qt, stage0, stage1, NoMask{});
+        tile_step(qt + 1, stage1, stage0, NoMask{});
+    }
+    if (qt < n_qt) tile_step(qt++, stage0, stage1, Mask{});
+    if (qt < n_qt) tile_step(qt++, stage1, stage0, Mask{});
 
     // epilogue: lane holds key `key`, d = db*32 + 8i + 4g + j in register 4i + j
     if (key < N) {
@@ -286,7 +363,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     constexpr int NKC = D / 16;
     constexpr int ND = D / 32;
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];   // 2 stages x (K, V)
+    // two stages (K tile, V tile), separate arrays as in the dK/dV kernel
+    __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
 
     const int nwg = gridDim.x;
     int wg = blockIdx.x;
@@ -404,16 +483,20 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
     using NoMask = std::integral_constant<bool, false>;
     using Mask = std::integral_constant<bool, true>;
-    uint16_t* const stage0 = smem;
-    uint16_t* const stage1 = smem + 2 * TILE;
+    uint16_t* const stage0 = smem0;
+    uint16_t* const stage1 = smem1;
     load_tile(0, stage0);
     int kt = 0;
     for (; kt < n_full; kt += 2) {
         tile_step(kt, stage0, stage1, NoMask{});
         if (kt + 1 < n_full) tile_step(kt + 1, stage1, stage0, NoMask{});
     }
-    for (kt = n_full; kt < n_kt; ++kt)
-        tile_step(kt, (kt & 1) ? stage1 : stage0, (kt & 1) ? stage0 : stage1, Mask{});
+    kt = n_full;
+    if (kt < n_kt && (kt & 1)) tile_step(kt++, stage1, stage0, Mask{});
+    for (; kt < n_kt; kt += 2) {
+        tile_step(kt, stage0, stage1, Mask{});
+        if (kt + 1 < n_kt) tile_step(kt + 1, stage1, stage0, Mask{});
+    }
 
     if (qrow < N) {
         uint16_t* dqrow = dQ + base + (size_t)qrow * D;

@@ -128,8 +128,13 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     constexpr int NKC = D / 16;                // S^T MFMAs along d
     constexpr int ND = D / 32;                 // 32-row blocks of O^T
 
-    // two stages, each a K tile followed by a V tile
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];
+    // two stages, each a K tile followed by a V tile.  The stages are separate
+    // arrays: the compiler then knows that reads of one stage do not alias the
+    // asynchronous HBM -> LDS loads into the other, and does not make them wait
+    // for those loads (with one array, every transposed read would wait for
+    // the next tile's loads to land).
+    __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
 
     // work group -> (batch*head, query block); XCD-aware remap (work groups are
     // dealt round-robin to 8 XCDs: give each XCD a contiguous range so the query
@@ -340,8 +345,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     //      an immediate), then the few masked tiles (ragged end, causal diagonal)
     using NoMask = std::integral_constant<bool, false>;
     using Mask = std::integral_constant<bool, true>;
-    uint16_t* const stage0 = smem;
-    uint16_t* const stage1 = smem + 2 * TILE;
+    uint16_t* const stage0 = smem0;
+    uint16_t* const stage1 = smem1;
+    // tile kt lives in stage kt & 1; every call names its stages statically
     load_tile(0, stage0);
     int kt = 0;
     for (; kt < n_full; kt += 2) {
@@ -349,10 +355,10 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         if (kt + 1 < n_full) tile_step(kt + 1, stage1, stage0, NoMask{});
     }
     kt = n_full;
-    for (; kt < n_kt; ++kt) {
-        uint16_t* cur = (kt & 1) ? stage1 : stage0;
-        uint16_t* nxt = (kt & 1) ? stage0 : stage1;
-        tile_step(kt, cur, nxt, Mask{});
+    if (kt < n_kt && (kt & 1)) tile_step(kt++, stage1, stage0, Mask{});
+    for (; kt < n_kt; kt += 2) {
+        tile_step(kt, stage0, stage1, Mask{});
+        if (kt + 1 < n_kt) tile_step(kt + 1, stage1, stage0, Mask{});
     }
 
     // ---- epilogue: O = O_acc / l (bf16, round to nearest even), LSE = ln l + m
