@@ -31,7 +31,10 @@ Readings where the pages are silent (all pinned by tests in tests/test_oracle.py
   * LSE is the natural log of sum_j exp(S_ij), with S already scaled;
   * causal is square with no offset: query i sees keys 0..i;
   * decode: the single query of a sequence sees all of its seq_len cached
-    tokens; seq_len <= 0 gives O = 0 and LSE = -inf (the empty sum).
+    tokens; seq_len <= 0 gives O = 0 and LSE = -inf (the empty sum);
+  * prefill over the paged cache: a sequence's new tokens are the last ones of
+    its seq_len cached tokens, so causal query i of n new ones sees positions
+    0 .. seq_len - n + i; a query that sees nothing gets O = 0, LSE = -inf.
 """
 from __future__ import annotations
 
@@ -40,7 +43,7 @@ import math
 import numpy as np
 
 __all__ = ["attention_fp64", "attention_bruteforce", "paged_gather_fp64", "paged_decode_fp64",
-           "attention_backward_fp64"]
+           "paged_prefill_fp64", "attention_backward_fp64"]
 
 
 def _as64(x) -> np.ndarray:
@@ -167,6 +170,58 @@ def paged_decode_fp64(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
         lse[n] = ll[0]
     if pairs is None:
         return o.reshape(S, H, d), lse.reshape(S, H)
+    return o, lse
+
+
+def paged_prefill_fp64(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *,
+                       causal: bool = True, scale: float | None = None, rows=None):
+    """A batch of sequences, each with new query tokens, against a paged KV cache, float64.
+
+    Sequence s holds ``L = seq_lens[s]`` cached tokens, read through its row of
+    the block table ("LLM study notes", section "Paged attention"); its new
+    tokens are the last ``n_s = cu_seqlens_q[s+1] - cu_seqlens_q[s]`` of them,
+    and their queries are rows ``cu_seqlens_q[s] ..`` of the packed ``q``.
+    Query i of the sequence stands at position ``L - n_s + i``; with ``causal``
+    it sees the keys at positions ``0 .. L - n_s + i`` (the current and earlier
+    tokens, "FlashAttention-2 GPU work partitioning", section 4), otherwise all
+    L keys.  A query that sees no key gets o = 0 and lse = -inf (the empty sum).
+
+    q: ``[total_q][H][d]``; caches ``[num_blocks][H][page_size][d]``;
+    block_table ``[S][max_blocks]``; seq_lens ``[S]``; cu_seqlens_q ``[S+1]``.
+    ``rows`` optionally lists packed query rows to compute (result in that
+    order).  Returns ``(o [R][H][d], lse [R][H])`` as float64.
+    """
+    q = _as64(q)
+    total_q, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    S = cu.size - 1
+    want = np.arange(total_q) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    o = np.zeros((want.size, H, d), dtype=np.float64)
+    lse = np.full((want.size, H), -np.inf, dtype=np.float64)
+    for s in range(S):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        sel = np.nonzero((want >= lo) & (want < hi))[0]
+        if sel.size == 0:
+            continue
+        L = int(seq_lens[s])
+        if L <= 0:
+            continue
+        i = want[sel] - lo                                  # index among the new tokens
+        pos = L - (hi - lo) + i                             # position of each query
+        keys = np.arange(L)
+        for h in range(H):
+            ks, vs = paged_gather_fp64(k_cache, v_cache, block_table, L, s, h)
+            sc = scale * (q[want[sel], h, :] @ ks.T)        # [rows, L]
+            if causal:
+                sc = np.where(keys[None, :] > pos[:, None], -np.inf, sc)
+            m = sc.max(axis=1, keepdims=True)
+            seen = np.isfinite(m[:, 0])
+            p = np.exp(sc[seen] - m[seen])
+            l = p.sum(axis=1, keepdims=True)
+            o[sel[seen], h] = (p @ vs) / l
+            lse[sel[seen], h] = (m[seen] + np.log(l))[:, 0]
     return o, lse
 
 
