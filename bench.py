@@ -11,8 +11,10 @@ One step = the whole hot path over one batch of synthetic input, resident in HBM
 forward calls over their kernel time, HIP events on the launch stream).  The
 decode's HBM GB/s, per-call figures, the roofline of the dominant kernel and
 the CPU oracle's rate on a bounded sample are reported in the same JSON line.
-The backward pass (fa_bwd) of both forward calls is timed after the steps, in
-a loop of its own, and reported under "bwd" (it is not part of the step).
+The backward pass (fa_bwd) of both forward calls and a paged prefill
+(fa_paged_prefill: 16 sequences with 0..4096 cached tokens receiving 256..1792
+new ones, H=32, d=128, causal) are timed after the steps, each in a loop of
+its own, and reported under "bwd" and "prefill" (they are not part of the step).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--skip-bwd]
 """
@@ -46,6 +48,22 @@ def bwd_flops(B, H, N, d, causal):
     (S recomputed, dP, dV, dQ, dK), 2.5x the forward's.  The dK/dV and dQ
     kernels recompute S and dP once more each; that extra work is not counted."""
     return 2.5 * fwd_flops(B, H, N, d, causal)
+
+
+def prefill_flops(wl, causal=True):
+    """Algorithmic FLOPs of a paged prefill: 4*d per (new query, visible key)
+    pair and head; causal query i of n new ones in a sequence of L tokens
+    sees L - n + i + 1 keys."""
+    L = wl.layout
+    pairs = 0
+    for s in range(L.S):
+        n, total = int(wl.new_lens[s]), int(L.seq_lens[s])
+        if causal:
+            first = total - n + 1
+            pairs += n * first + n * (n - 1) // 2
+        else:
+            pairs += n * total
+    return 4.0 * L.d * L.H * pairs
 
 
 def decode_bytes(layout):
@@ -119,8 +137,9 @@ def main():
     ap.add_argument("--skip-decode", action="store_true",
                     help="forward only (for profiling the forward kernel alone)")
     ap.add_argument("--skip-bwd", action="store_true", help="do not time the backward pass")
+    ap.add_argument("--skip-prefill", action="store_true", help="do not time the paged prefill")
     ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode", "bwd-noncausal",
-                                       "bwd-causal"],
+                                       "bwd-causal", "prefill"],
                     help="run one call per step (for per-kernel counter runs)")
     ap.add_argument("--probe-copy", type=int, metavar="MIB",
                     help="instead of the hot path, copy a buffer of MIB MiB a few times "
@@ -260,8 +279,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops_nc, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops_nc / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("fwd_bf16_kernel<128,1,false> B=8 H=16 N=2048"),
-                     "kernel": "fwd_bf16_kernel<128,1,false>",
+                     "traffic": measured_traffic("fwd_bf16_kernel<128,false> B=8 H=16 N=2048"),
+                     "kernel": "fwd_bf16_kernel<128,false>",
                      "flops_per_launch": f_nc},
     }
     if decode:
@@ -308,9 +327,54 @@ def main():
                                f"{tag}_frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         out["bwd"]["flops"] = "2.5x forward (10 N^2 d per head non-causal)"
 
+    # ---- paged prefill, its own timed loop ----
+    t_pre = None
+    if not args.skip_prefill and args.only in (None, "prefill"):
+        wl = w.prefill_workload(**w.PREFILL_P1)
+        Lp = wl.layout
+        qp = torch.from_numpy(w.prefill_q(wl)).to(dev).to(torch.bfloat16)
+        ppools = []
+        for which in ("k", "v"):
+            pool = torch.empty((Lp.num_blocks, Lp.H, Lp.page_size, Lp.d), dtype=torch.bfloat16,
+                               device=dev)
+
+            def putp(lo, hi, x, pool=pool):
+                pool[lo:hi].copy_(torch.from_numpy(x).to(dev))
+            w.decode_pool(Lp, which, poison=False, chunk_callback=putp)
+            ppools.append(pool)
+        btp = torch.from_numpy(Lp.block_table).to(dev)
+        slp = torch.from_numpy(Lp.seq_lens).to(dev)
+        cup = torch.from_numpy(wl.cu_seqlens_q).to(dev)
+        op_ = torch.empty_like(qp)
+        lsep = torch.empty((wl.total_q, Lp.H), dtype=torch.float32, device=dev)
+
+        def pcall():
+            fa.fa_paged_prefill(qp, ppools[0], ppools[1], btp, slp, cup, op_, lsep, wl.max_q_len,
+                                True, Lp.scale)
+        for _ in range(args.warmup):
+            pcall()
+        torch.cuda.synchronize()
+        evp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        tot = 0.0
+        for _ in range(args.steps):
+            evp[0].record(stream)
+            pcall()
+            evp[1].record(stream)
+            evp[1].synchronize()
+            tot += evp[0].elapsed_time(evp[1])
+        t_pre = tot / args.steps
+        fl = prefill_flops(wl, True)
+        tf = fl / (t_pre * 1e-3) / 1e12
+        out["prefill"] = {"ms": round(t_pre, 4), "tflops": round(tf, 2),
+                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "causal": True,
+                          "new_tokens": wl.total_q, "cached_tokens": int(Lp.seq_lens.sum()),
+                          "flops": fl}
+        log("prefill timed")
+
     if args.only is not None:
         ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,
-              "bwd-noncausal": t_bwd.get(False), "bwd-causal": t_bwd.get(True)}[args.only]
+              "bwd-noncausal": t_bwd.get(False), "bwd-causal": t_bwd.get(True),
+              "prefill": t_pre}[args.only]
         print(json.dumps({"only": args.only, "ms": ms}), flush=True)
         return
     if not args.no_cpu_baseline:

@@ -1,0 +1,366 @@
+// fa_fwd_block.h - the bf16 attention forward of one block of 128 query rows
+// against one head's keys, for gfx950.  Used by the dense forward
+// (fa_fwd_bf16.hip) and by the paged prefill (fa_prefill.hip); they differ
+// only in where the query rows and the K/V tiles live, which a "K/V source"
+// (DenseKV, PagedKV) and a few row pointers describe.
+//
+// Per block: O = softmax(scale * Q K^T) V over the keys each query may see and
+// the natural-log log-sum-exp of every row, with the tiled online softmax of
+// "Flash Attention" (velog @myungum, section 2 and its pseudocode): key/value
+// tiles staged through on-chip memory, a running row maximum and row sum
+// rescaling the output accumulator, the score matrix never leaving the chip.
+// The work group owns its 128 rows of O ("FlashAttention-2 GPU work
+// partitioning", iPLEX blog, section 3).
+//
+// gfx950 mapping
+//  * 4 waves x 32 query rows.  All of a wave's state fits in 256 VGPRs, so
+//    two work groups share a CU and one wave's softmax overlaps the other's
+//    MFMAs.
+//  * K and V tiles (64 keys) go HBM -> LDS with buffer_load ... lds (no
+//    register staging), double-buffered in two separate LDS arrays, one
+//    barrier per tile; rows are stored with their 16-byte chunks XOR-swizzled
+//    (swz), which makes the K reads and the transposed V reads conflict-free.
+//  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
+//    Q in registers as the B operand): a lane holds one query and 16 keys, so
+//    row max / row sum are in-lane plus one v_permlane32_swap.
+//  * O^T += V^T P^T: the probabilities, converted to bf16, are already the B
+//    operand; V^T comes from the row-major V tile via ds_read_b64_tr_b16.
+//  * p = 2^(c*s - c*m) with c = |scale| log2(e) in one FMA; the accumulator
+//    is rescaled only when a row maximum grows by more than 2^8 (a
+//    wave-uniform branch), and normalised once at the end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_gfx950.h"
+
+namespace fa_gfx950 {
+
+constexpr int kFwdBN = TILE_ROWS;              // keys per tile
+constexpr int kFwdWaves = 4;
+constexpr int kFwdThreads = kFwdWaves * 64;
+constexpr int kFwdBM = kFwdWaves * 32;         // query rows per work group
+constexpr float kRescaleThreshold = 8.0f;      // log2 units
+
+template <int D>
+struct FwdShape {
+    static constexpr int TILE = kFwdBN * D;                       // elements per K or V tile
+    static constexpr int LPW = TILE * 2 / 1024 / kFwdWaves;       // 1 KiB loads per wave per tensor
+    static constexpr int NKC = D / 16;                            // S^T MFMAs along d
+    static constexpr int ND = D / 32;                             // 32-row blocks of O^T
+};
+
+// K/V of one head stored densely, [rows][D]; tile kt = rows 64kt .. 64kt+63.
+// Buffer resources span the head, so rows past the end arrive as zeros.
+template <int D>
+struct DenseKV {
+    static constexpr bool kPaged = false;
+    const uint16_t* K;
+    const uint16_t* V;
+    int len;                                   // keys
+    int gofs[FwdShape<D>::LPW];                // this lane's byte offset in the tile, per load
+
+    __device__ __forceinline__ void setup(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < FwdShape<D>::LPW; ++i)
+            gofs[i] = tile_load_offset<D>(wave * FwdShape<D>::LPW + i, lane);
+    }
+    // Issue tile kt's loads into `stage` (K tile, then V tile).  Returns the
+    // tile's pages that must be hidden (none here).
+    __device__ __forceinline__ uint32_t load(int kt, uint16_t* stage, int wave) const {
+        constexpr int LPW = FwdShape<D>::LPW;
+        const int bytes = len * D * 2;
+        const int tb = kt * kFwdBN * D * 2;
+        load_tile_lds<LPW>(K, bytes, tb, &gofs[0], stage, wave * LPW);
+        load_tile_lds<LPW>(V, bytes, tb, &gofs[0], stage + FwdShape<D>::TILE, wave * LPW);
+        return 0u;
+    }
+};
+
+// K/V of one head of one sequence in a paged cache [num_blocks][H][16][D],
+// logical page p of the sequence at physical page table[p].  A 64-key tile is
+// 4 pages and wave w loads page w of it (its LPW loads cover exactly 16 rows).
+// Slots past the sequence's length are never read (the buffer resource of a
+// page ends at its last valid row: the rest arrives as zeros), and a table
+// entry outside [0, num_blocks) is not followed: the page arrives as zeros
+// and the caller hides its keys.
+template <int D>
+struct PagedKV {
+    static constexpr bool kPaged = true;
+    static constexpr int kPage = 16;
+    const uint16_t* Kc;
+    const uint16_t* Vc;
+    const int32_t* table;                      // this sequence's row of the block table
+    int64_t num_blocks;
+    int64_t page_stride;                       // elements per physical page (H * 16 * D)
+    int64_t head_off;                          // elements to this head inside a page (h * 16 * D)
+    int len;                                   // keys (cached tokens of the sequence)
+    int gofs[FwdShape<D>::LPW];                // byte offset inside this wave's page, per load
+
+    __device__ __forceinline__ void setup(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < FwdShape<D>::LPW; ++i)
+            gofs[i] = tile_load_offset<D>(wave * FwdShape<D>::LPW + i, lane) - wave * kPage * D * 2;
+    }
+    // Physical page of logical page p, or -1 when p is past the sequence or
+    // the entry is out of range (wave-uniform: scalar loads).
+    __device__ __forceinline__ int64_t page(int p) const {
+        const int n_pages = (len + kPage - 1) / kPage;
+        if (p >= n_pages) return -1;
+        const int64_t id = table[p];
+        return (id >= 0 && id < num_blocks) ? id : -1;
+    }
+    __device__ __forceinline__ uint32_t load(int kt, uint16_t* stage, int wave) const {
+        constexpr int LPW = FwdShape<D>::LPW;
+        const int n_pages = (len + kPage - 1) / kPage;
+        uint32_t hide = 0u;
+        int64_t mine = -1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int p = 4 * kt + w;
+            const int64_t id = page(p);
+            if (p < n_pages && id < 0) hide |= 1u << w;
+            if (w == wave) mine = id;
+        }
+        const int rows = (mine < 0) ? 0 : min(kPage, len - (4 * kt + wave) * kPage);
+        const int64_t off = (mine < 0 ? 0 : mine) * page_stride + head_off;
+        const int bytes = rows * D * 2;
+        load_tile_lds<LPW>(Kc + off, bytes, 0, &gofs[0], stage, wave * LPW);
+        load_tile_lds<LPW>(Vc + off, bytes, 0, &gofs[0], stage + FwdShape<D>::TILE, wave * LPW);
+        return hide;
+    }
+};
+
+// Query rows of the block: row r (0-based in the sequence / head) at
+// Q + r * stride; O the same; LSE at lse + r * lse_stride (lse may be null).
+struct QRows {
+    const uint16_t* Q;
+    uint16_t* O;
+    float* lse;
+    int64_t stride;                            // elements between consecutive rows
+    int64_t lse_stride;
+    int rows;                                  // valid rows
+};
+
+// One block of kFwdBM query rows starting at row q0.  Causal: row r sees the
+// keys 0 .. shift + r (shift = 0 for square attention; for new tokens at the
+// end of a sequence of kv.len tokens, shift = kv.len - rows).  A row that sees
+// no key gets O = 0 and LSE = -inf.
+template <int D, bool CAUSAL, class KV>
+__device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, const QRows& qr,
+                                          KV& kv, int q0, int shift, float scale_log2) {
+    using Sh = FwdShape<D>;
+    constexpr int TILE = Sh::TILE;
+    constexpr int NKC = Sh::NKC;
+    constexpr int ND = Sh::ND;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int wq0 = q0 + wave * 32;            // first query row of this wave
+    const int qrow = wq0 + l32;                // this lane's query row
+    const int N = kv.len;
+
+    // Scores are kept raw: p = 2^(c*s - c*m).  c = 0 (scale 0) is replaced by
+    // 2^-100: every finite c*s then rounds to 0 in the exponent, so all visible
+    // keys get p = 1 exactly as with c = 0, while hidden keys (s = -inf) still
+    // get p = 0 without a separate test.
+    const float c = fmaxf(fabsf(scale_log2), 7.888609052210118e-31f);
+    const uint32_t qflip = (scale_log2 < 0.f) ? 0x80008000u : 0u;   // fold a negative scale into Q
+    const float tau_raw = (c > 0.f) ? kRescaleThreshold / c : __builtin_inff();
+
+    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
+    bf16x8 qop[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (qrow < qr.rows)
+            x = *reinterpret_cast<const u32x4*>(qr.Q + qrow * qr.stride + kc * 16 + g * 8);
+        x ^= qflip;
+        qop[kc] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+
+    // ---- tiles: causal blocks stop at the last key their last row sees;
+    //      tiles before n_full need no mask (every key exists and is seen by
+    //      every row of the block)
+    const int n_kt_all = (N + kFwdBN - 1) / kFwdBN;
+    int n_kt = n_kt_all, n_full = N / kFwdBN;
+    if (CAUSAL) {
+        const int last = shift + min(qr.rows, q0 + kFwdBM) - 1;   // last key any row sees
+        n_kt = last < 0 ? 0 : min(n_kt_all, last / kFwdBN + 1);
+        const int first = shift + q0;                             // last key the first row sees
+        n_full = first < kFwdBN - 1 ? 0 : min(n_full, (first + 1) / kFwdBN);
+    }
+    n_full = min(n_full, n_kt);
+
+    kv.setup(wave, lane);
+    uint32_t hide_next = 0u;                   // pages of the next tile to hide (paged)
+
+    // ---- per-lane LDS offsets (elements) of the MFMA operand reads; the row
+    //      offsets 32kb (+16cc, +8) do not change the swizzle, so they and the
+    //      stage offset are immediates.
+    int kofs[NKC];                             // K fragment, key row l32, chunk 2kc+g
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) kofs[kc] = frag_offset<D>(l32, 2 * kc + g);
+    int vofs[2][ND];                           // V transpose read, key row 4g+li/4 (+8)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) vofs[hl][db] = trfrag_offset<D>(lane, hl, db * 32);
+
+    // ---- one key tile: wait for its loads, sync (all loads landed, everyone
+    //      is done with the other buffer), start the next tile's loads into
+    //      the other buffer, then scores, online softmax and PV on this one.
+    auto tile_step = [&](int kt, uint16_t* cur, uint16_t* nxt, auto mask_tag) __device__
+        __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const uint16_t* ks = cur;
+        const uint16_t* vs = cur + TILE;
+        const uint32_t hide = hide_next;
+        __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads have landed
+        __syncthreads();
+        if (kt + 1 < n_kt) hide_next = kv.load(kt + 1, nxt, wave);
+        const int k0 = kt * kFwdBN;
+        if (MASK && CAUSAL && k0 > shift + wq0 + 31) return;   // tile after all of this wave's keys
+
+        // ---- S^T = K Q^T for 2 blocks of 32 keys
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + kofs[kc]));
+                sacc[kb] = mfma(a, qop[kc], sacc[kb]);
+            }
+        {
+            // schedule: keep four K fragment reads (DS read, 0x100) in flight
+            // ahead of the score MFMAs (0x008)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * NKC - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+
+        // ---- online softmax; lane holds query qrow and keys
+        //      k0 + 32kb + 8(r/4) + 4g + r%4 (page 2kb + r/8 of the tile)
+        if constexpr (KV::kPaged) {
+            if (hide != 0u) {                  // rare: a page the table does not resolve
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if ((hide >> (2 * kb + (r >> 3))) & 1u) sacc[kb][r] = kNegInf;
+            }
+        }
+        if constexpr (MASK) {                  // ragged end of the keys or causal diagonal:
+            // hide key k0 + 4g + off(kb, r) when it is past this row's last key
+            const int lim = (CAUSAL ? min(N - 1, shift + qrow) : N - 1) - (k0 + 4 * g);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = kNegInf;
+        }
+        float mt = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+        mt = pair_max(mt);
+        if (__any(mt > m_run + tau_raw)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+        bf16x8 pop[2][2];
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
+                if (r & 1) ps1 += p; else ps0 += p;
+                pop[kb][r >> 3][r & 7] = (__bf16)p;
+            }
+        l_run += ps0 + ps1;                    // row sum from the fp32 probabilities
+
+        // ---- O^T += V^T P^T.  Fragment for d rows db*32 .. +32 and keys
+        //      32kb + 16cc + {4g..4g+3, 8+4g..8+4g+3}: two transpose loads.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const uint16_t* vb = vs + (kb * 32 + cc * 16) * D;
+#pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    const bf16x8 a = tr_operand(vb + vofs[0][db], vb + vofs[1][db]);
+                    oacc[db] = mfma(a, pop[kb][cc], oacc[db]);
+                }
+            }
+    };
+
+    // ---- tile loops: unmasked tiles unrolled by two (each body's LDS stage is
+    //      named statically), then the few masked tiles (ragged end, causal
+    //      diagonal); tile kt lives in stage kt & 1.
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+    if (n_kt > 0) hide_next = kv.load(0, smem0, wave);
+    int kt = 0;
+    for (; kt < n_full; kt += 2) {
+        tile_step(kt, smem0, smem1, NoMask{});
+        if (kt + 1 < n_full) tile_step(kt + 1, smem1, smem0, NoMask{});
+    }
+    kt = n_full;
+    if (kt < n_kt && (kt & 1)) tile_step(kt++, smem1, smem0, Mask{});
+    for (; kt < n_kt; kt += 2) {
+        tile_step(kt, smem0, smem1, Mask{});
+        if (kt + 1 < n_kt) tile_step(kt + 1, smem1, smem0, Mask{});
+    }
+
+    // ---- epilogue: O = O_acc / l (bf16, round to nearest even), LSE = ln l + m;
+    //      a row that saw no key (l = 0) gets O = 0, LSE = -inf
+    const float l_tot = pair_sum(l_run);
+    if (qrow < qr.rows) {
+        const bool empty = !(l_tot > 0.f);
+        const float inv = empty ? 0.f : 1.0f / l_tot;
+        uint16_t* orow = qr.O + qrow * qr.stride;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * i + 4 * g) =
+                    to_bf16x4(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv,
+                              oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+        if (qr.lse != nullptr && g == 0) {
+            const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+            qr.lse[qrow * qr.lse_stride] = empty ? kNegInf : (mc + __log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
+}  // namespace fa_gfx950

@@ -1,0 +1,114 @@
+// fa_prefill.hip - bf16 prefill of new tokens against a paged KV cache, gfx950.
+//
+// A batch of sequences of different lengths: sequence s has seq_lens[s]
+// cached tokens in fixed-size pages reached through its row of the block
+// table ("LLM study notes", DEVOCEAN tech blog, section "Paged attention"),
+// and its last n_s tokens are new, with their queries packed at rows
+// cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1.  Every new query attends to the
+// cached tokens it may see (causal: those up to its own position), computed
+// FlashAttention-style: paged memory with flash compute, the combination
+// "PagedAttention vs FlashAttention: key differences" recommends.  The block
+// computation is fwd_block (fa_fwd_block.h) over a paged K/V source: each
+// 64-key tile is 4 pages, one per wave, loaded HBM -> LDS through per-page
+// buffer resources that end at the sequence's last token.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_fwd_block.h"
+#include "fa_kernels.h"
+
+namespace {
+
+using namespace fa_gfx950;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kFwdThreads, 2)
+void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
+                         const uint16_t* __restrict__ Vc, const int32_t* __restrict__ table,
+                         const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
+                         uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int max_blocks,
+                         int64_t num_blocks, int total_q, int n_qblocks, float scale_log2) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * FwdShape<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
+
+    // work group -> (sequence, head, query block), query blocks of a
+    // (sequence, head) adjacent and kept on one XCD; causal: longest rows first
+    const int nwg = gridDim.x;
+    int wg = blockIdx.x;
+    if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+    const int per_seq = n_qblocks * H;
+    const int s = wg / per_seq;
+    const int rem = wg - s * per_seq;
+    const int h = rem / n_qblocks;
+    int qb = rem - h * n_qblocks;
+    if (CAUSAL) qb = n_qblocks - 1 - qb;
+
+    // this sequence's new rows, kept inside [0, total_q)
+    const int qbeg = cu_q[s];
+    int rows = cu_q[s + 1] - qbeg;
+    if (qbeg < 0 || qbeg >= total_q) rows = 0;
+    rows = max(0, min(rows, total_q - qbeg));
+    const int q0 = qb * kFwdBM;
+    if (q0 >= rows) return;                    // whole work group: no row here
+    const int L = max(0, min(seq_lens[s], max_blocks * PagedKV<D>::kPage));
+
+    PagedKV<D> kv;
+    kv.Kc = Kc;
+    kv.Vc = Vc;
+    kv.table = table + (size_t)s * max_blocks;
+    kv.num_blocks = num_blocks;
+    kv.page_stride = (int64_t)H * PagedKV<D>::kPage * D;
+    kv.head_off = (int64_t)h * PagedKV<D>::kPage * D;
+    kv.len = L;
+    QRows qr;
+    qr.Q = Q + ((int64_t)qbeg * H + h) * D;
+    qr.O = O + ((int64_t)qbeg * H + h) * D;
+    qr.lse = LSE != nullptr ? LSE + (int64_t)qbeg * H + h : nullptr;
+    qr.stride = (int64_t)H * D;
+    qr.lse_stride = H;
+    qr.rows = rows;
+    // the new tokens are the last `rows` of the L cached ones
+    fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, q0, L - rows, scale_log2);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* table,
+                  const int32_t* seq_lens, const int32_t* cu_q, void* o, float* lse, int S, int H,
+                  int max_blocks, int64_t num_blocks, int total_q, int max_q_len, float scale,
+                  hipStream_t stream) {
+    const int n_qblocks = (max_q_len + kFwdBM - 1) / kFwdBM;
+    const unsigned nwg = (unsigned)S * (unsigned)H * (unsigned)n_qblocks;
+    const uint16_t* qp = static_cast<const uint16_t*>(q);
+    const uint16_t* kp = static_cast<const uint16_t*>(k_cache);
+    const uint16_t* vp = static_cast<const uint16_t*>(v_cache);
+    uint16_t* op = static_cast<uint16_t*>(o);
+    float scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    void* args[] = {&qp, &kp, &vp, (void*)&table, (void*)&seq_lens, (void*)&cu_q, &op, &lse,
+                    &H, &max_blocks, &num_blocks, &total_q, (void*)&n_qblocks, &scale_log2};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_bf16_kernel<D, CAUSAL>),
+                           dim3(nwg), dim3(kFwdThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t fa_launch_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* cu_seqlens_q, void* o, float* lse, int S, int H,
+                                   int d, int max_blocks, int64_t num_blocks, int total_q,
+                                   int max_q_len, int causal, float scale, hipStream_t stream) {
+    if (d == 128)
+        return causal ? launch<128, true>(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
+                                          o, lse, S, H, max_blocks, num_blocks, total_q, max_q_len,
+                                          scale, stream)
+                      : launch<128, false>(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
+                                           o, lse, S, H, max_blocks, num_blocks, total_q, max_q_len,
+                                           scale, stream);
+    if (d == 64)
+        return causal ? launch<64, true>(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
+                                         o, lse, S, H, max_blocks, num_blocks, total_q, max_q_len,
+                                         scale, stream)
+                      : launch<64, false>(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
+                                          o, lse, S, H, max_blocks, num_blocks, total_q, max_q_len,
+                                          scale, stream);
+    return hipErrorInvalidValue;
+}

@@ -109,6 +109,31 @@ inline fa_status check_decode(const void* q, const void* kc, const void* vc, con
     return FA_OK;
 }
 
+inline fa_status check_prefill(const void* q, const void* kc, const void* vc, const void* table,
+                               const void* lens, const void* cu, const void* o, int S, int H,
+                               int d, int page_size, int max_blocks, int64_t num_blocks,
+                               int total_q, int max_q_len, int causal, float scale, int dtype) {
+    if (!q || !kc || !vc || !table || !lens || !cu || !o) return FA_ERR_INVALID;
+    if (S < 1 || H < 1 || d < 1 || page_size < 1 || max_blocks < 1 || num_blocks < 1 ||
+        total_q < 1 || max_q_len < 1)
+        return FA_ERR_INVALID;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID;
+    const double pool = double(num_blocks) * H * page_size * d;
+    if (pool >= 4611686018427387904.0) return FA_ERR_INVALID;            // 2^62 elements
+    if (double(total_q) * H * d >= 4611686018427387904.0) return FA_ERR_INVALID;
+    if (double(S) * max_blocks >= 2147483647.0) return FA_ERR_INVALID;   // int32 table index
+    if (double(max_blocks) * page_size >= 2147483647.0) return FA_ERR_INVALID;
+    // one work group per (sequence, head, block of kFwdBlockM new rows)
+    const double groups = double(S) * H * std::ceil(double(max_q_len) / kFwdBlockM);
+    if (groups > 2147483647.0) return FA_ERR_INVALID;
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!fwd_head_dim_supported(d)) return FA_ERR_UNSUPPORTED;
+    if (page_size != kDecodePageSize) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
 inline const char* status_string(int s) {
     switch (s) {
         case FA_OK: return "FA_OK";

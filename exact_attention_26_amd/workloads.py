@@ -32,7 +32,7 @@ __all__ = [
     "FwdConfig", "FWD_CONFIGS", "round_to_bf16", "fwd_inputs",
     "DecodeLayout", "decode_layout", "decode_q", "decode_pool", "decode_pool_pages",
     "page_valid_slots", "fwd_config_inputs", "bwd_dout",
-    "DECODE_C4",
+    "DECODE_C4", "PrefillWorkload", "prefill_workload", "prefill_q", "PREFILL_P1",
 ]
 
 
@@ -233,6 +233,62 @@ def decode_layout(seed: int, *, S: int = 64, H: int = 32, d: int = 128, page_siz
 
 DECODE_C4 = dict(S=64, H=32, d=128, page_size=16, len_range=(128, 8192), shared_prefix=512,
                  spare=64, seed=4)
+
+
+@dataclass
+class PrefillWorkload:
+    """New tokens of ``S`` sequences against a paged KV cache.
+
+    ``layout.seq_lens[s]`` counts all cached tokens of sequence s, its new
+    ones included (they are the last ``new_lens[s]``); the queries of the new
+    tokens are packed ``[total_q][H][d]``, sequence s at rows
+    ``cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1``.
+    """
+    layout: DecodeLayout
+    new_lens: np.ndarray          # int32 [S]
+    cu_seqlens_q: np.ndarray      # int32 [S+1]
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.new_lens.max(initial=0))
+
+
+def prefill_workload(seed: int, *, S: int = 16, H: int = 32, d: int = 128, page_size: int = 16,
+                     ctx_range=(0, 4096), new_range=(256, 1792), ctx_lens=None, new_lens=None,
+                     shared_prefix: int = 0, spare: int = 16) -> PrefillWorkload:
+    """Draw context and new-token counts (uniform, inclusive ranges, from
+    ``default_rng([seed, 7])``) unless given, then lay the pages out as the
+    decode workload does (shuffled pool, optional shared prefixes, spare and
+    poison pages)."""
+    rng = np.random.default_rng([seed, 7])
+    ctx = (rng.integers(ctx_range[0], ctx_range[1] + 1, S) if ctx_lens is None
+           else np.asarray(ctx_lens, dtype=np.int64))
+    new = (rng.integers(new_range[0], new_range[1] + 1, S) if new_lens is None
+           else np.asarray(new_lens, dtype=np.int64))
+    lens = ctx + new
+    max_blocks = max(1, int(-(-int(lens.max(initial=1)) // page_size)))
+    layout = decode_layout(seed, S=S, H=H, d=d, page_size=page_size, lens=lens,
+                           len_range=(0, int(lens.max(initial=1))), shared_prefix=shared_prefix,
+                           spare=spare, max_blocks=max_blocks)
+    cu = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    return PrefillWorkload(layout=layout, new_lens=new.astype(np.int32), cu_seqlens_q=cu)
+
+
+def prefill_q(w: PrefillWorkload, dtype: str = "bf16") -> np.ndarray:
+    """Queries of the new tokens, ``[total_q][H][d]`` float32 (stream ``[seed, 3]``)."""
+    rng = np.random.default_rng([w.layout.seed, 3])
+    x = rng.standard_normal((w.total_q, w.layout.H, w.layout.d), dtype=np.float32)
+    return round_to_bf16(x) if dtype == "bf16" else x
+
+
+# prefill benchmark: 16 sequences with 0..4096 cached tokens each receive
+# 256..1792 new ones (about 16k new tokens in all), H=32, d=128, pages of 16
+PREFILL_P1 = dict(S=16, H=32, d=128, page_size=16, ctx_range=(0, 4096), new_range=(256, 1792),
+                  seed=5)
 
 
 def decode_q(layout: DecodeLayout, dtype: str = "bf16") -> np.ndarray:

@@ -1,7 +1,7 @@
 /*
  * fa.h - C ABI of libfa.so: exact scaled-dot-product attention on MI355X (gfx950).
  *
- * Three operations sit behind this interface.
+ * Four operations sit behind this interface.
  *
  *   fa_fwd           the attention forward pass computed FlashAttention-style:
  *                    Q, K, V in device memory, O (and the per-row log-sum-exp)
@@ -11,6 +11,9 @@
  *   fa_paged_decode  one query token per sequence attending to a KV cache that
  *                    is stored in fixed-size pages and reached through a block
  *                    table.
+ *   fa_paged_prefill the new tokens of a batch of sequences of different
+ *                    lengths attending to that paged cache (prefill, chunked
+ *                    prefill, continuous batching).
  *
  * What is computed.  For every batch b and head h, with s_ij = scale * q_i . k_j
  * over the keys j that query i may see (all j, or j <= i when causal):
@@ -204,6 +207,57 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
                           int max_blocks_per_seq, int64_t num_blocks, float scale,
                           int dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * fa_paged_prefill - new query tokens of several sequences against a paged KV cache.
+ *
+ * Continuous batching mixes sequences of different lengths in one call
+ * ("LLM study notes", DEVOCEAN tech blog, batching section), and the paged
+ * cache and FlashAttention-style compute are used together ("PagedAttention
+ * vs FlashAttention: key differences"): K/V are read through the block table
+ * ("LLM study notes", section "Paged attention") in tiles of 64 keys, with
+ * the online softmax of fa_fwd.  Sequence s has seq_lens[s] cached tokens,
+ * INCLUDING its new ones, which are the last n_s = cu_seqlens_q[s+1] -
+ * cu_seqlens_q[s] of them (their K/V must already be in the cache).  New
+ * query i of sequence s stands at position seq_lens[s] - n_s + i; causal = 1
+ * lets it see positions 0 .. seq_lens[s] - n_s + i (the current and earlier
+ * tokens, "FlashAttention-2 GPU work partitioning", iPLEX blog, section 4),
+ * causal = 0 lets it see all seq_lens[s] tokens.
+ *
+ *   q            [total_q][H][d] bf16, sequence s at rows cu_seqlens_q[s] ..  (read)
+ *   k_cache      [num_blocks][H][page_size][d] bf16                          (read)
+ *   v_cache      [num_blocks][H][page_size][d] bf16                          (read)
+ *   block_table  [S][max_blocks_per_seq] int32 physical page ids             (read)
+ *   seq_lens     [S] int32 cached tokens per sequence, new ones included     (read)
+ *   cu_seqlens_q [S+1] int32, cu_seqlens_q[0] = 0, non-decreasing,
+ *                cu_seqlens_q[S] = total_q                                   (read)
+ *   o            [total_q][H][d] bf16                                        (written)
+ *   lse          [total_q][H] float32 natural-log log-sum-exp, or NULL       (written)
+ *   num_seqs (S), H >= 1;  d: 64 or 128;  page_size: 16;  max_blocks_per_seq >= 1;
+ *   num_blocks >= 1;  total_q >= 1;  max_q_len >= 1 and >= every n_s (rows of
+ *   a sequence past max_q_len are not written);  causal 0 or 1;  scale finite;
+ *   dtype FA_BF16 (FA_F32 -> FA_ERR_UNSUPPORTED).  No workspace.
+ *
+ * Device-resident inputs are not inspected on the host; their out-of-range
+ * values have defined results:
+ *   a query that sees no token (seq_lens[s] <= 0, or causal with
+ *   n_s > seq_lens[s] for its first n_s - seq_lens[s] queries)  -> o = 0, lse = -inf
+ *   seq_lens[s] > max_blocks_per_seq * page_size -> clamped to that many tokens
+ *   a block_table entry outside [0, num_blocks) -> that page's tokens are not seen
+ *   rows cu_seqlens_q[s] .. that fall outside [0, total_q) -> not written
+ *   table entries past page ceil(seq_lens[s]/page_size)-1 and cache slots past
+ *   seq_lens[s] in the last page are never read.
+ *
+ * Returns FA_OK, FA_ERR_INVALID (null required pointer, sizes < 1, causal not
+ * 0/1, non-finite scale, more than 2^31-1 work groups), FA_ERR_UNSUPPORTED
+ * (d, page_size or dtype), or FA_ERR_HIP.
+ */
+fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* cu_seqlens_q, void* o, float* lse,
+                           int num_seqs, int H, int d, int page_size, int max_blocks_per_seq,
+                           int64_t num_blocks, int total_q, int max_q_len, int causal,
+                           float scale, int dtype, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);

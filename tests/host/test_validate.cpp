@@ -117,6 +117,32 @@ int main() {
     EXPECT_EQ(check_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 1, 96, 0, 1.f, FA_BF16, p, 1024),
               FA_ERR_UNSUPPORTED);
 
+    // prefill: valid
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 16, 32, 128, 16, 319, 3262, 15516, 1651, 1,
+                            0.088f, FA_BF16), FA_OK);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 1, 1, 0, -1.f, FA_BF16),
+              FA_OK);
+    // prefill: invalid
+    EXPECT_EQ(check_prefill(p, p, p, p, p, nullptr, p, 1, 1, 64, 16, 1, 1, 1, 1, 0, 1.f, FA_BF16),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 0, 1, 0, 1.f, FA_BF16),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 1, 0, 0, 1.f, FA_BF16),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 1, 1, 3, 1.f, FA_BF16),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 65535, 65535, 64, 16, 1, 1, 1, 129, 0, 1.f,
+                            FA_BF16), FA_ERR_INVALID);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 1, 1, 0, nan, FA_BF16),
+              FA_ERR_INVALID);
+    // prefill: unsupported
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 96, 16, 1, 1, 1, 1, 0, 1.f, FA_BF16),
+              FA_ERR_UNSUPPORTED);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 32, 1, 1, 1, 1, 0, 1.f, FA_BF16),
+              FA_ERR_UNSUPPORTED);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 1, 1, 0, 1.f, FA_F32),
+              FA_ERR_UNSUPPORTED);
+
     EXPECT_EQ(std::string_view(status_string(FA_OK)).size() > 0, 1);
     if (failures) {
         std::fprintf(stderr, "%d check(s) failed\n", failures);

@@ -24,7 +24,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted([
         "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
-        "fa_paged_decode_workspace_size", "fa_status_string", "fa_last_hip_error"])
+        "fa_paged_decode_workspace_size", "fa_paged_prefill", "fa_status_string",
+        "fa_last_hip_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -118,6 +119,27 @@ def _decode(**kw):
 ])
 def test_decode_rejects_before_launch(kw, status):
     assert _decode(**kw) == status
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, o=FAKE, lse=None, S=2, H=2,
+             d=128, P=16, mb=4, nb=10, tq=30, mq=20, causal=1, scale=0.1, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.load_library().fa_paged_prefill(
+        a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["cu"], a["o"], a["lse"], a["S"], a["H"],
+        a["d"], a["P"], a["mb"], a["nb"], a["tq"], a["mq"], a["causal"], a["scale"], a["dtype"],
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(bt=None), 1),
+    (dict(sl=None), 1), (dict(cu=None), 1), (dict(o=None), 1), (dict(S=0), 1), (dict(H=0), 1),
+    (dict(mb=0), 1), (dict(nb=0), 1), (dict(tq=0), 1), (dict(mq=0), 1), (dict(causal=2), 1),
+    (dict(scale=float("inf")), 1), (dict(S=65536, H=65536), 1),
+    (dict(d=96), 2), (dict(P=8), 2), (dict(dtype=fa.FA_F32), 2), (dict(dtype=3), 2),
+])
+def test_prefill_rejects_before_launch(kw, status):
+    assert _prefill(**kw) == status
 
 
 def test_host_validation_unit_with_sanitizers(tmp_path):
