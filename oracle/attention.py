@@ -34,7 +34,10 @@ Readings where the pages are silent (all pinned by tests in tests/test_oracle.py
     tokens; seq_len <= 0 gives O = 0 and LSE = -inf (the empty sum);
   * prefill over the paged cache: a sequence's new tokens are the last ones of
     its seq_len cached tokens, so causal query i of n new ones sees positions
-    0 .. seq_len - n + i; a query that sees nothing gets O = 0, LSE = -inf.
+    0 .. seq_len - n + i; a query that sees nothing gets O = 0, LSE = -inf;
+  * tree attention (speculative decoding): a draft tree's node sees the
+    committed tokens and the nodes on its own path from the root (its
+    ancestors and itself), nothing else of the tree.
 """
 from __future__ import annotations
 
@@ -43,7 +46,7 @@ import math
 import numpy as np
 
 __all__ = ["attention_fp64", "attention_bruteforce", "paged_gather_fp64", "paged_decode_fp64",
-           "paged_prefill_fp64", "attention_backward_fp64"]
+           "paged_prefill_fp64", "tree_ancestors", "tree_decode_fp64", "attention_backward_fp64"]
 
 
 def _as64(x) -> np.ndarray:
@@ -222,6 +225,69 @@ def paged_prefill_fp64(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
             l = p.sum(axis=1, keepdims=True)
             o[sel[seen], h] = (p @ vs) / l
             lse[sel[seen], h] = (m[seen] + np.log(l))[:, 0]
+    return o, lse
+
+
+def tree_ancestors(parents) -> list:
+    """For each node of a draft tree, the set of nodes on its path from the
+    root: itself, its parent, its parent's parent, ...  ``parents[i]`` is the
+    index of node i's parent among the tree's nodes, or -1 when node i hangs
+    directly off the committed tokens.  Nodes come parents-first
+    (``parents[i] < i``); a parent index outside ``[0, i)`` is taken as -1.
+    """
+    out = []
+    for i, p in enumerate(int(x) for x in parents):
+        path = {i}
+        while 0 <= p < i and p not in path:
+            path.add(p)
+            p = int(parents[p]) if 0 <= int(parents[p]) < p else -1
+        out.append(path)
+    return out
+
+
+def tree_decode_fp64(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, parents, *,
+                     scale: float | None = None):
+    """Verification of a draft token tree in one pass, float64.
+
+    "LLM study notes" (DEVOCEAN tech blog), speculative decoding section: a
+    draft model proposes candidate tokens organised as a tree, each node one
+    token, and the target model computes all nodes in a single forward pass
+    with tree attention.  Here sequence s holds ``L = seq_lens[s]`` cached
+    tokens read through its block table ("Paged attention" section); its
+    ``n = cu_seqlens_q[s+1] - cu_seqlens_q[s]`` tree nodes are the last n of
+    them, in node order, and their queries are rows ``cu_seqlens_q[s] ..`` of
+    ``q``.  Node i sees the L - n committed tokens and the nodes of its own
+    path from the root (``tree_ancestors``); ``parents`` is packed like ``q``.
+
+    Returns ``(o [total_q][H][d], lse [total_q][H])``; a node that sees
+    nothing gets o = 0, lse = -inf.
+    """
+    q = _as64(q)
+    total_q, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    o = np.zeros((total_q, H, d), dtype=np.float64)
+    lse = np.full((total_q, H), -np.inf, dtype=np.float64)
+    for s in range(cu.size - 1):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        n, L = hi - lo, int(seq_lens[s])
+        if n <= 0 or L <= 0:
+            continue
+        ctx = L - n
+        paths = tree_ancestors(np.asarray(parents)[lo:hi])
+        for h in range(H):
+            ks, vs = paged_gather_fp64(k_cache, v_cache, block_table, L, s, h)
+            for i in range(n):
+                seen = [t for t in range(L) if t < ctx or (t - ctx) in paths[i]]
+                seen = [t for t in seen if t >= 0]
+                if not seen:
+                    continue
+                sc = scale * (ks[seen] @ q[lo + i, h])
+                m = sc.max()
+                p = np.exp(sc - m)
+                o[lo + i, h] = (p @ vs[seen]) / p.sum()
+                lse[lo + i, h] = m + np.log(p.sum())
     return o, lse
 
 
