@@ -11,10 +11,12 @@ One step = the whole hot path over one batch of synthetic input, resident in HBM
 forward calls over their kernel time, HIP events on the launch stream).  The
 decode's HBM GB/s, per-call figures, the roofline of the dominant kernel and
 the CPU oracle's rate on a bounded sample are reported in the same JSON line.
-The backward pass (fa_bwd) of both forward calls and a paged prefill
+The backward pass (fa_bwd) of both forward calls, a paged prefill
 (fa_paged_prefill: 16 sequences with 0..4096 cached tokens receiving 256..1792
-new ones, H=32, d=128, causal) are timed after the steps, each in a loop of
-its own, and reported under "bwd" and "prefill" (they are not part of the step).
+new ones, H=32, d=128, causal) and a draft-tree verification (fa_tree_decode:
+64 sequences of 128..8192 committed tokens, 64-node trees, H=32, d=128) are
+timed after the steps, each in a loop of its own, and reported under "bwd",
+"prefill" and "tree" (they are not part of the step).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--skip-bwd]
 """
@@ -64,6 +66,29 @@ def prefill_flops(wl, causal=True):
         else:
             pairs += n * total
     return 4.0 * L.d * L.H * pairs
+
+
+def tree_work(wl, parents):
+    """Algorithmic FLOPs and HBM bytes of a tree verification: 4*d flops per
+    (node, visible key) pair and head; bytes = every distinct (page, head) row
+    any node sees (K and V, shared pages once) plus q, o, lse, the used table
+    entries, seq_lens, cu_seqlens_q and the parents."""
+    from exact_attention_26_amd.workloads import page_valid_slots
+    L = wl.layout
+    pairs = 0
+    for s in range(L.S):
+        lo, hi = int(wl.cu_seqlens_q[s]), int(wl.cu_seqlens_q[s + 1])
+        ctx = int(L.seq_lens[s]) - (hi - lo)
+        depth = []                             # nodes on each node's path from the root
+        for i in range(hi - lo):
+            p = int(parents[lo + i])
+            depth.append(1 + (depth[p] if 0 <= p < i else 0))
+        pairs += sum(ctx + k for k in depth)
+    flops = 4.0 * L.d * L.H * pairs
+    kv = float(page_valid_slots(L).sum()) * L.H * L.d * 2 * 2
+    pages_used = sum(L.used_pages(s).size for s in range(L.S))
+    small = wl.total_q * L.H * (L.d * 2 * 2 + 4) + pages_used * 4 + L.S * 8 + wl.total_q * 4
+    return flops, kv + small
 
 
 def decode_bytes(layout):
@@ -138,8 +163,9 @@ def main():
                     help="forward only (for profiling the forward kernel alone)")
     ap.add_argument("--skip-bwd", action="store_true", help="do not time the backward pass")
     ap.add_argument("--skip-prefill", action="store_true", help="do not time the paged prefill")
+    ap.add_argument("--skip-tree", action="store_true", help="do not time the tree verification")
     ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode", "bwd-noncausal",
-                                       "bwd-causal", "prefill"],
+                                       "bwd-causal", "prefill", "tree"],
                     help="run one call per step (for per-kernel counter runs)")
     ap.add_argument("--probe-copy", type=int, metavar="MIB",
                     help="instead of the hot path, copy a buffer of MIB MiB a few times "
@@ -371,10 +397,56 @@ def main():
                           "flops": fl}
         log("prefill timed")
 
+    # ---- draft-tree verification, its own timed loop ----
+    t_tree = None
+    if not args.skip_tree and args.only in (None, "tree"):
+        wlt, part = w.tree_workload(**w.TREE_T1)
+        Lt = wlt.layout
+        qt_ = torch.from_numpy(w.prefill_q(wlt)).to(dev).to(torch.bfloat16)
+        tpools = []
+        for which in ("k", "v"):
+            pool = torch.empty((Lt.num_blocks, Lt.H, Lt.page_size, Lt.d), dtype=torch.bfloat16,
+                               device=dev)
+
+            def putt(lo, hi, x, pool=pool):
+                pool[lo:hi].copy_(torch.from_numpy(x).to(dev))
+            w.decode_pool(Lt, which, poison=False, chunk_callback=putt)
+            tpools.append(pool)
+        btt = torch.from_numpy(Lt.block_table).to(dev)
+        slt = torch.from_numpy(Lt.seq_lens).to(dev)
+        cut = torch.from_numpy(wlt.cu_seqlens_q).to(dev)
+        prt = torch.from_numpy(part).to(dev)
+        ot = torch.empty_like(qt_)
+        lset = torch.empty((wlt.total_q, Lt.H), dtype=torch.float32, device=dev)
+
+        def tcall():
+            fa.fa_tree_decode(qt_, tpools[0], tpools[1], btt, slt, cut, prt, ot, lset,
+                              wlt.max_q_len, Lt.scale)
+        for _ in range(args.warmup):
+            tcall()
+        torch.cuda.synchronize()
+        evt = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        tot = 0.0
+        for _ in range(args.steps):
+            evt[0].record(stream)
+            tcall()
+            evt[1].record(stream)
+            evt[1].synchronize()
+            tot += evt[0].elapsed_time(evt[1])
+        t_tree = tot / args.steps
+        fl, by = tree_work(wlt, part)
+        out["tree"] = {"ms": round(t_tree, 4),
+                       "tflops": round(fl / (t_tree * 1e-3) / 1e12, 2),
+                       "hbm_gbs": round(by / (t_tree * 1e-3) / 1e9, 1),
+                       "hbm_frac_peak": round(by / (t_tree * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "nodes": wlt.total_q, "committed_tokens": int(Lt.seq_lens.sum()) - wlt.total_q,
+                       "flops": fl, "algorithmic_bytes": by}
+        log("tree timed")
+
     if args.only is not None:
         ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,
               "bwd-noncausal": t_bwd.get(False), "bwd-causal": t_bwd.get(True),
-              "prefill": t_pre}[args.only]
+              "prefill": t_pre, "tree": t_tree}[args.only]
         print(json.dumps({"only": args.only, "ms": ms}), flush=True)
         return
     if not args.no_cpu_baseline:

@@ -59,6 +59,10 @@ def load_library():
     lib.fa_paged_prefill.argtypes = [c.c_void_p] * 8 + [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int,
                                                         c.c_int64, c.c_int, c.c_int, c.c_int,
                                                         c.c_float, c.c_int, c.c_void_p]
+    lib.fa_tree_decode.restype = c.c_int
+    lib.fa_tree_decode.argtypes = [c.c_void_p] * 9 + [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int,
+                                                      c.c_int64, c.c_int, c.c_int, c.c_float,
+                                                      c.c_int, c.c_void_p]
     lib.fa_status_string.restype = c.c_char_p
     lib.fa_status_string.argtypes = [c.c_int]
     lib.fa_last_hip_error.restype = c.c_int
@@ -244,6 +248,44 @@ def fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o
         raise FaError(st, "fa_paged_prefill")
 
 
+def fa_tree_decode(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, tree_parents, o,
+                   lse, max_q_len: int, scale: float) -> None:
+    """Call ``fa_tree_decode``: as ``fa_paged_prefill`` plus ``tree_parents``
+    (int32 [total_q], each node's parent among its sequence's nodes or -1)."""
+    torch = _torch()
+    _check_dense("tree_parents", tree_parents, q.device)
+    if tree_parents.dtype != torch.int32 or tuple(tree_parents.shape) != (q.shape[0],):
+        raise ValueError("tree_parents must be int32 [total_q]")
+    total_q, H, d = q.shape
+    nb, Hk, P, dk = k_cache.shape
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens),
+                    ("cu_seqlens_q", cu_seqlens_q), ("o", o)):
+        _check_dense(name, t, dev)
+    if (Hk, dk) != (H, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [num_blocks][H][page_size][d]")
+    S = block_table.shape[0]
+    if any(t.dtype != torch.int32 for t in (block_table, seq_lens, cu_seqlens_q)):
+        raise ValueError("block_table, seq_lens and cu_seqlens_q must be int32")
+    if block_table.dim() != 2 or tuple(seq_lens.shape) != (S,) \
+            or tuple(cu_seqlens_q.shape) != (S + 1,):
+        raise ValueError("block_table must be [S][max_blocks], seq_lens [S], cu_seqlens_q [S+1]")
+    if tuple(o.shape) != (total_q, H, d) or o.dtype != q.dtype:
+        raise ValueError("o must match q")
+    if lse is not None:
+        _check_dense("lse", lse, dev)
+        if tuple(lse.shape) != (total_q, H) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [total_q][H]")
+    st = load_library().fa_tree_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(cu_seqlens_q), _ptr(tree_parents), _ptr(o), _ptr(lse), S, H, d, P,
+        block_table.shape[1], nb, total_q, int(max_q_len), float(scale), _dtype_code(q),
+        _stream(dev))
+    if st != FA_OK:
+        raise FaError(st, "fa_tree_decode")
+
+
 # --------------------------------------------------------------------------
 # convenience wrappers that allocate outputs with torch
 # --------------------------------------------------------------------------
@@ -285,6 +327,20 @@ def paged_prefill(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, max_
     lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
     fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse,
                      max_q_len, causal, scale)
+    return o, lse
+
+
+def tree_decode(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, tree_parents,
+                max_q_len: int, scale: float | None = None):
+    """Draft-tree verification against a paged KV cache.  Returns ``(o, lse)``."""
+    torch = _torch()
+    total_q, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
+    fa_tree_decode(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, tree_parents, o, lse,
+                   max_q_len, scale)
     return o, lse
 
 

@@ -81,6 +81,23 @@ fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cac
                                               causal, scale, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_tree_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* cu_seqlens_q, const int32_t* tree_parents, void* o,
+                         float* lse, int num_seqs, int H, int d, int page_size,
+                         int max_blocks_per_seq, int64_t num_blocks, int total_q, int max_q_len,
+                         float scale, int dtype, void* stream) {
+    const fa_status st = fa_host::check_tree(q, k_cache, v_cache, block_table, seq_lens,
+                                             cu_seqlens_q, tree_parents, o, num_seqs, H, d,
+                                             page_size, max_blocks_per_seq, num_blocks, total_q,
+                                             max_q_len, scale, dtype);
+    if (st != FA_OK) return st;
+    return hip_status(fa_launch_tree_decode(q, k_cache, v_cache, block_table, seq_lens,
+                                            cu_seqlens_q, tree_parents, o, lse, num_seqs, H, d,
+                                            max_blocks_per_seq, num_blocks, total_q, scale,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_string(int status) { return fa_host::status_string(status); }
 
 int fa_last_hip_error(void) { return t_last_hip_error; }

@@ -1,8 +1,9 @@
 // fa_fwd_block.h - the bf16 attention forward of one block of 128 query rows
 // against one head's keys, for gfx950.  Used by the dense forward
-// (fa_fwd_bf16.hip) and by the paged prefill (fa_prefill.hip); they differ
-// only in where the query rows and the K/V tiles live, which a "K/V source"
-// (DenseKV, PagedKV) and a few row pointers describe.
+// (fa_fwd_bf16.hip), the paged prefill and the draft-tree verification
+// (fa_prefill.hip); they differ only in where the query rows and the K/V
+// tiles live, which a "K/V source" (DenseKV, PagedKV) and a few row pointers
+// describe, and in the mask (none, causal, tree).
 //
 // Per block: O = softmax(scale * Q K^T) V over the keys each query may see and
 // the natural-log log-sum-exp of every row, with the tiled online softmax of
@@ -145,13 +146,22 @@ struct QRows {
     int rows;                                  // valid rows
 };
 
+// Largest draft tree of the tree mode (one 64-bit path mask per node).
+constexpr int kMaxTreeNodes = 64;
+
 // One block of kFwdBM query rows starting at row q0.  Causal: row r sees the
 // keys 0 .. shift + r (shift = 0 for square attention; for new tokens at the
-// end of a sequence of kv.len tokens, shift = kv.len - rows).  A row that sees
-// no key gets O = 0 and LSE = -inf.
-template <int D, bool CAUSAL, class KV>
+// end of a sequence of kv.len tokens, shift = kv.len - rows).  TREE: the rows
+// are the nodes of a draft tree whose K/V are the last `rows` keys; row r
+// sees the keys before `shift` (the committed tokens) and the tree keys of
+// the nodes on its path from the root, found by walking `parents` (node r's
+// parent among the rows, or -1; parents come first).  A row that sees no key
+// gets O = 0 and LSE = -inf.
+template <int D, bool CAUSAL, class KV, bool TREE = false>
 __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, const QRows& qr,
-                                          KV& kv, int q0, int shift, float scale_log2) {
+                                          KV& kv, int q0, int shift, float scale_log2,
+                                          const int32_t* parents = nullptr) {
+    static_assert(!(CAUSAL && TREE), "the tree mask replaces the causal mask");
     using Sh = FwdShape<D>;
     constexpr int TILE = Sh::TILE;
     constexpr int NKC = Sh::NKC;
@@ -191,11 +201,28 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
+    // ---- tree mode: bit j of `path` = this row may see tree node j (itself
+    //      and its ancestors; the walk ends because parents precede children)
+    uint64_t path = 0;
+    if constexpr (TREE) {
+        if (qrow < qr.rows && qrow < kMaxTreeNodes) {
+            path = 1ull << qrow;
+            int cur = qrow;
+            int p = parents[qrow];
+            while (p >= 0 && p < cur) {
+                path |= 1ull << p;
+                cur = p;
+                p = parents[p];
+            }
+        }
+    }
+
     // ---- tiles: causal blocks stop at the last key their last row sees;
     //      tiles before n_full need no mask (every key exists and is seen by
     //      every row of the block)
     const int n_kt_all = (N + kFwdBN - 1) / kFwdBN;
     int n_kt = n_kt_all, n_full = N / kFwdBN;
+    if (TREE) n_full = min(n_full, max(shift, 0) / kFwdBN);   // tiles of committed tokens only
     if (CAUSAL) {
         const int last = shift + min(qr.rows, q0 + kFwdBM) - 1;   // last key any row sees
         n_kt = last < 0 ? 0 : min(n_kt_all, last / kFwdBN + 1);
@@ -232,6 +259,7 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
         __syncthreads();
         if (kt + 1 < n_kt) hide_next = kv.load(kt + 1, nxt, wave);
         const int k0 = kt * kFwdBN;
+        if (wq0 >= qr.rows) return;            // no row of this wave exists
         if (MASK && CAUSAL && k0 > shift + wq0 + 31) return;   // tile after all of this wave's keys
 
         // ---- S^T = K Q^T for 2 blocks of 32 keys
@@ -279,6 +307,17 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = kNegInf;
+            if constexpr (TREE) {              // tree keys: only the row's path
+                const int t0 = k0 + 4 * g - shift;     // tree node of the lane's first key
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int t = t0 + kb * 32 + 8 * (r >> 2) + (r & 3);
+                        if (t >= 0 && (t >= kMaxTreeNodes || !((path >> t) & 1ull)))
+                            sacc[kb][r] = kNegInf;
+                    }
+            }
         }
         float mt = kNegInf;
 #pragma unroll

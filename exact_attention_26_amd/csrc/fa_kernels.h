@@ -28,6 +28,14 @@ hipError_t fa_launch_paged_prefill(const void* q, const void* k_cache, const voi
                                    int d, int max_blocks, int64_t num_blocks, int total_q,
                                    int max_q_len, int causal, float scale, hipStream_t stream);
 
+// bf16 draft-tree verification against a paged KV cache (fa_prefill.hip)
+hipError_t fa_launch_tree_decode(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* cu_seqlens_q, const int32_t* parents, void* o,
+                                 float* lse, int S, int H, int d, int max_blocks,
+                                 int64_t num_blocks, int total_q, float scale,
+                                 hipStream_t stream);
+
 hipError_t fa_launch_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   void* o, float* lse, int S, int H, int d,

@@ -1,4 +1,5 @@
-// fa_prefill.hip - bf16 prefill of new tokens against a paged KV cache, gfx950.
+// fa_prefill.hip - bf16 prefill of new tokens, and verification of a draft
+// token tree, against a paged KV cache, gfx950.
 //
 // A batch of sequences of different lengths: sequence s has seq_lens[s]
 // cached tokens in fixed-size pages reached through its row of the block
@@ -71,6 +72,56 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, q0, L - rows, scale_log2);
 }
 
+// Draft-tree verification ("LLM study notes", speculative decoding section:
+// the target model computes every node of the draft tree in one pass with
+// tree attention): the rows of sequence s are the nodes of its draft tree,
+// whose K/V are the last n_s cached tokens; node i sees the committed tokens
+// and the nodes on its path from the root.  One work group per (sequence,
+// head); at most kMaxTreeNodes nodes, rows past that are not written.
+template <int D>
+__global__ __launch_bounds__(kFwdThreads, 2)
+void tree_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
+                      const uint16_t* __restrict__ Vc, const int32_t* __restrict__ table,
+                      const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
+                      const int32_t* __restrict__ parents, uint16_t* __restrict__ O,
+                      float* __restrict__ LSE, int H, int max_blocks, int64_t num_blocks,
+                      int total_q, float scale_log2) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * FwdShape<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
+
+    const int nwg = gridDim.x;
+    int wg = blockIdx.x;
+    if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+    const int s = wg / H;
+    const int h = wg - s * H;
+
+    const int qbeg = cu_q[s];
+    int rows = cu_q[s + 1] - qbeg;
+    if (qbeg < 0 || qbeg >= total_q) rows = 0;
+    rows = max(0, min(min(rows, total_q - qbeg), kMaxTreeNodes));
+    if (rows == 0) return;
+    const int L = max(0, min(seq_lens[s], max_blocks * PagedKV<D>::kPage));
+
+    PagedKV<D> kv;
+    kv.Kc = Kc;
+    kv.Vc = Vc;
+    kv.table = table + (size_t)s * max_blocks;
+    kv.num_blocks = num_blocks;
+    kv.page_stride = (int64_t)H * PagedKV<D>::kPage * D;
+    kv.head_off = (int64_t)h * PagedKV<D>::kPage * D;
+    kv.len = L;
+    QRows qr;
+    qr.Q = Q + ((int64_t)qbeg * H + h) * D;
+    qr.O = O + ((int64_t)qbeg * H + h) * D;
+    qr.lse = LSE != nullptr ? LSE + (int64_t)qbeg * H + h : nullptr;
+    qr.stride = (int64_t)H * D;
+    qr.lse_stride = H;
+    qr.rows = rows;
+    // the tree's K/V are the last `rows` of the L cached tokens
+    fwd_block<D, false, PagedKV<D>, true>(smem0, smem1, qr, kv, 0, L - rows, scale_log2,
+                                          parents + qbeg);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* table,
                   const int32_t* seq_lens, const int32_t* cu_q, void* o, float* lse, int S, int H,
@@ -90,6 +141,30 @@ hipError_t launch(const void* q, const void* k_cache, const void* v_cache, const
 }
 
 }  // namespace
+
+hipError_t fa_launch_tree_decode(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* cu_seqlens_q, const int32_t* parents, void* o,
+                                 float* lse, int S, int H, int d, int max_blocks,
+                                 int64_t num_blocks, int total_q, float scale,
+                                 hipStream_t stream) {
+    const uint16_t* qp = static_cast<const uint16_t*>(q);
+    const uint16_t* kp = static_cast<const uint16_t*>(k_cache);
+    const uint16_t* vp = static_cast<const uint16_t*>(v_cache);
+    uint16_t* op = static_cast<uint16_t*>(o);
+    float scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    void* args[] = {&qp, &kp, &vp, (void*)&block_table, (void*)&seq_lens, (void*)&cu_seqlens_q,
+                    (void*)&parents, &op, &lse, &H, &max_blocks, &num_blocks, &total_q,
+                    &scale_log2};
+    const dim3 grid((unsigned)S * (unsigned)H);
+    if (d == 128)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&tree_bf16_kernel<128>), grid,
+                               dim3(kFwdThreads), args, 0, stream);
+    if (d == 64)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&tree_bf16_kernel<64>), grid,
+                               dim3(kFwdThreads), args, 0, stream);
+    return hipErrorInvalidValue;
+}
 
 hipError_t fa_launch_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* seq_lens,

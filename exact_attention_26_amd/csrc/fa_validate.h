@@ -134,6 +134,23 @@ inline fa_status check_prefill(const void* q, const void* kc, const void* vc, co
     return FA_OK;
 }
 
+// Draft-tree verification: at most this many nodes per tree.
+constexpr int kTreeMaxNodes = 64;
+
+inline fa_status check_tree(const void* q, const void* kc, const void* vc, const void* table,
+                            const void* lens, const void* cu, const void* parents, const void* o,
+                            int S, int H, int d, int page_size, int max_blocks,
+                            int64_t num_blocks, int total_q, int max_q_len, float scale,
+                            int dtype) {
+    if (!parents) return FA_ERR_INVALID;
+    const fa_status st = check_prefill(q, kc, vc, table, lens, cu, o, S, H, d, page_size,
+                                       max_blocks, num_blocks, total_q, max_q_len, 0, scale,
+                                       dtype);
+    if (st != FA_OK) return st;
+    if (max_q_len > kTreeMaxNodes) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
 inline const char* status_string(int s) {
     switch (s) {
         case FA_OK: return "FA_OK";

@@ -33,6 +33,7 @@ __all__ = [
     "DecodeLayout", "decode_layout", "decode_q", "decode_pool", "decode_pool_pages",
     "page_valid_slots", "fwd_config_inputs", "bwd_dout",
     "DECODE_C4", "PrefillWorkload", "prefill_workload", "prefill_q", "PREFILL_P1",
+    "tree_parents", "tree_workload", "TREE_T1",
 ]
 
 
@@ -289,6 +290,41 @@ def prefill_q(w: PrefillWorkload, dtype: str = "bf16") -> np.ndarray:
 # 256..1792 new ones (about 16k new tokens in all), H=32, d=128, pages of 16
 PREFILL_P1 = dict(S=16, H=32, d=128, page_size=16, ctx_range=(0, 4096), new_range=(256, 1792),
                   seed=5)
+
+
+def tree_parents(seed: int, new_lens, *, max_back: int = 8) -> np.ndarray:
+    """Packed parent indices of one random draft tree per sequence, int32.
+
+    Node 0 hangs off the committed tokens (-1); node i > 0 takes a parent
+    uniformly among the ``max_back`` nodes before it, or -1 (another root)
+    when the draw falls before node 0.  Parents precede children.  Stream
+    ``default_rng([seed, 9])``.
+    """
+    rng = np.random.default_rng([seed, 9])
+    out = []
+    for n in np.asarray(new_lens, dtype=np.int64):
+        par = np.empty(int(n), dtype=np.int32)
+        for i in range(int(n)):
+            par[i] = -1 if i == 0 else max(-1, int(rng.integers(i - max_back, i)))
+        out.append(par)
+    return np.concatenate(out) if out else np.zeros(0, np.int32)
+
+
+def tree_workload(seed: int, *, S: int = 64, H: int = 32, d: int = 128, page_size: int = 16,
+                  ctx_range=(128, 8192), nodes: int = 64, ctx_lens=None, new_lens=None,
+                  shared_prefix: int = 512, spare: int = 64):
+    """Draft trees of ``nodes`` nodes appended to contexts drawn as the decode
+    workload draws its lengths; returns ``(PrefillWorkload, parents)``."""
+    new = np.full(S, nodes, dtype=np.int64) if new_lens is None else new_lens
+    wl = prefill_workload(seed, S=S, H=H, d=d, page_size=page_size, ctx_range=ctx_range,
+                          new_range=(nodes, nodes), ctx_lens=ctx_lens, new_lens=new,
+                          shared_prefix=shared_prefix, spare=spare)
+    return wl, tree_parents(seed, wl.new_lens)
+
+
+# tree verification benchmark: 64 sequences with 128..8192 committed tokens
+# (pairs sharing a 512-token prefix) each verify a 64-node draft tree, H=32, d=128
+TREE_T1 = dict(S=64, H=32, d=128, page_size=16, ctx_range=(128, 8192), nodes=64, seed=6)
 
 
 def decode_q(layout: DecodeLayout, dtype: str = "bf16") -> np.ndarray:

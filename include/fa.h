@@ -1,7 +1,7 @@
 /*
  * fa.h - C ABI of libfa.so: exact scaled-dot-product attention on MI355X (gfx950).
  *
- * Four operations sit behind this interface.
+ * Five operations sit behind this interface.
  *
  *   fa_fwd           the attention forward pass computed FlashAttention-style:
  *                    Q, K, V in device memory, O (and the per-row log-sum-exp)
@@ -14,6 +14,8 @@
  *   fa_paged_prefill the new tokens of a batch of sequences of different
  *                    lengths attending to that paged cache (prefill, chunked
  *                    prefill, continuous batching).
+ *   fa_tree_decode   the nodes of a draft token tree per sequence attending to
+ *                    that paged cache under a tree mask (speculative decoding).
  *
  * What is computed.  For every batch b and head h, with s_ij = scale * q_i . k_j
  * over the keys j that query i may see (all j, or j <= i when causal):
@@ -258,6 +260,45 @@ fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cac
                            int num_seqs, int H, int d, int page_size, int max_blocks_per_seq,
                            int64_t num_blocks, int total_q, int max_q_len, int causal,
                            float scale, int dtype, void* stream);
+
+/*
+ * fa_tree_decode - verify a draft token tree per sequence in one pass.
+ *
+ * Speculative decoding ("LLM study notes", DEVOCEAN tech blog, speculative
+ * decoding section): a draft model proposes candidate tokens organised as a
+ * tree, each node one token, and the target model computes every node in a
+ * single forward pass with tree attention.  Here sequence s has seq_lens[s]
+ * cached tokens whose last n_s = cu_seqlens_q[s+1] - cu_seqlens_q[s] are the
+ * tree's nodes in node order (their K/V already in the cache); node i sees
+ * the seq_lens[s] - n_s committed tokens and the nodes on its own path from
+ * the root -- itself, its parent, its parent's parent, ... -- and no other
+ * node (no siblings, no descendants).  K/V are read through the block table
+ * ("LLM study notes", section "Paged attention") with the tiled online
+ * softmax of fa_fwd.
+ *
+ *   q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse,
+ *   num_seqs, H, d, page_size, max_blocks_per_seq, num_blocks, total_q, scale,
+ *   dtype, stream    as in fa_paged_prefill
+ *   tree_parents     [total_q] int32, packed like q: the index (0-based among
+ *                    the sequence's nodes) of node i's parent, which must be
+ *                    smaller than i, or -1 when node i hangs directly off the
+ *                    committed tokens                                    (read)
+ *   max_q_len        >= every n_s and at most 64 (else FA_ERR_UNSUPPORTED):
+ *                    one work group per (sequence, head) holds the whole tree
+ *
+ * Device-resident inputs: a parent index outside [0, i) is taken as -1;
+ * nodes past the 64th of a sequence are not written; the rest as in
+ * fa_paged_prefill (a node that sees no token gets o = 0, lse = -inf).
+ *
+ * Returns FA_OK, FA_ERR_INVALID (as fa_paged_prefill, or tree_parents NULL),
+ * FA_ERR_UNSUPPORTED (d, page_size, dtype, or max_q_len > 64), or FA_ERR_HIP.
+ */
+fa_status fa_tree_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* cu_seqlens_q, const int32_t* tree_parents,
+                         void* o, float* lse, int num_seqs, int H, int d, int page_size,
+                         int max_blocks_per_seq, int64_t num_blocks, int total_q, int max_q_len,
+                         float scale, int dtype, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);

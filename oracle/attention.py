@@ -276,17 +276,23 @@ def tree_decode_fp64(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, p
             continue
         ctx = L - n
         paths = tree_ancestors(np.asarray(parents)[lo:hi])
+        # keys node i sees: the committed tokens, then its path's tree tokens
+        seen_of = [np.concatenate([np.arange(max(ctx, 0)),
+                                   np.array(sorted(ctx + j for j in paths[i] if 0 <= ctx + j < L),
+                                            dtype=np.int64)]).astype(np.int64)
+                   for i in range(n)]
         for h in range(H):
             ks, vs = paged_gather_fp64(k_cache, v_cache, block_table, L, s, h)
+            scores = scale * (ks @ q[lo:hi, h].T)             # [L, n]: every key, every node
             for i in range(n):
-                seen = [t for t in range(L) if t < ctx or (t - ctx) in paths[i]]
-                seen = [t for t in seen if t >= 0]
-                if not seen:
+                seen = seen_of[i]
+                if seen.size == 0:
                     continue
-                sc = scale * (ks[seen] @ q[lo + i, h])
+                sc = scores[seen, i]
                 m = sc.max()
-                p = np.exp(sc - m)
-                o[lo + i, h] = (p @ vs[seen]) / p.sum()
+                p = np.zeros(L)                                # unseen keys weigh nothing
+                p[seen] = np.exp(sc - m)
+                o[lo + i, h] = (p @ vs) / p.sum()
                 lse[lo + i, h] = m + np.log(p.sum())
     return o, lse
 

@@ -143,6 +143,14 @@ int main() {
     EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 1, 1, 0, 1.f, FA_F32),
               FA_ERR_UNSUPPORTED);
 
+    // tree: valid, then a missing parent array, then a tree too large
+    EXPECT_EQ(check_tree(p, p, p, p, p, p, p, p, 64, 32, 128, 16, 520, 14707, 4096, 64, 0.088f,
+                         FA_BF16), FA_OK);
+    EXPECT_EQ(check_tree(p, p, p, p, p, p, nullptr, p, 64, 32, 128, 16, 520, 14707, 4096, 64,
+                         0.088f, FA_BF16), FA_ERR_INVALID);
+    EXPECT_EQ(check_tree(p, p, p, p, p, p, p, p, 64, 32, 128, 16, 520, 14707, 4096, 65, 0.088f,
+                         FA_BF16), FA_ERR_UNSUPPORTED);
+
     EXPECT_EQ(std::string_view(status_string(FA_OK)).size() > 0, 1);
     if (failures) {
         std::fprintf(stderr, "%d check(s) failed\n", failures);

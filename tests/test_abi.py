@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted([
         "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
         "fa_paged_decode_workspace_size", "fa_paged_prefill", "fa_status_string",
-        "fa_last_hip_error"])
+        "fa_last_hip_error", "fa_tree_decode"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -140,6 +140,24 @@ def _prefill(**kw):
 ])
 def test_prefill_rejects_before_launch(kw, status):
     assert _prefill(**kw) == status
+
+
+def _tree(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, par=FAKE, o=FAKE, lse=None,
+             S=2, H=2, d=128, P=16, mb=4, nb=10, tq=30, mq=20, scale=0.1, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.load_library().fa_tree_decode(
+        a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["cu"], a["par"], a["o"], a["lse"], a["S"],
+        a["H"], a["d"], a["P"], a["mb"], a["nb"], a["tq"], a["mq"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(par=None), 1), (dict(q=None), 1), (dict(cu=None), 1), (dict(S=0), 1), (dict(tq=0), 1),
+    (dict(mq=0), 1), (dict(scale=float("nan")), 1),
+    (dict(mq=65), 2), (dict(d=96), 2), (dict(P=32), 2), (dict(dtype=fa.FA_F32), 2),
+])
+def test_tree_rejects_before_launch(kw, status):
+    assert _tree(**kw) == status
 
 
 def test_host_validation_unit_with_sanitizers(tmp_path):
