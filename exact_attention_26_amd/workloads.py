@@ -33,7 +33,7 @@ __all__ = [
     "DecodeLayout", "decode_layout", "decode_q", "decode_pool", "decode_pool_pages",
     "page_valid_slots", "fwd_config_inputs", "bwd_dout",
     "DECODE_C4", "PrefillWorkload", "prefill_workload", "prefill_q", "PREFILL_P1",
-    "tree_parents", "tree_workload", "TREE_T1",
+    "tree_parents", "tree_workload", "TREE_T1", "rope_tables",
 ]
 
 
@@ -136,6 +136,17 @@ def bwd_dout(B: int, H: int, N: int, d: int, *, seed: int, dtype: str = "bf16",
     if dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return x
+
+
+def rope_tables(n_pos: int, d: int, base: float = 10000.0):
+    """Cosine and sine tables ``[n_pos][d/2]`` float32 of the usual rotary
+    frequencies: pair i of position p turns by p * base^(-2i/d) radians
+    (angles formed in float64, then rounded once to float32).  The tables are
+    inputs of the RoPE path; any other frequency schedule is just another table."""
+    i = np.arange(d // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / d)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 # --------------------------------------------------------------------------

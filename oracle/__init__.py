@@ -5,5 +5,6 @@ HIP path and imports nothing from it.
 """
 from .attention import (  # noqa: F401
     attention_backward_fp64, attention_bruteforce, attention_fp64, paged_decode_fp64,
-    paged_gather_fp64, paged_prefill_fp64, tree_ancestors, tree_decode_fp64,
+    paged_gather_fp64, paged_prefill_fp64, tree_ancestors, tree_decode_fp64, rope_fp64,
+    attention_rope_fp64,
 )

@@ -37,7 +37,10 @@ Readings where the pages are silent (all pinned by tests in tests/test_oracle.py
     0 .. seq_len - n + i; a query that sees nothing gets O = 0, LSE = -inf;
   * tree attention (speculative decoding): a draft tree's node sees the
     committed tokens and the nodes on its own path from the root (its
-    ancestors and itself), nothing else of the tree.
+    ancestors and itself), nothing else of the tree;
+  * RoPE: consecutive pairs (x[2i], x[2i+1]) of a row form one complex
+    number, rotated by the angle whose cosine and sine the caller's tables
+    hold for the row's position and pair i.
 """
 from __future__ import annotations
 
@@ -46,7 +49,8 @@ import math
 import numpy as np
 
 __all__ = ["attention_fp64", "attention_bruteforce", "paged_gather_fp64", "paged_decode_fp64",
-           "paged_prefill_fp64", "tree_ancestors", "tree_decode_fp64", "attention_backward_fp64"]
+           "paged_prefill_fp64", "tree_ancestors", "tree_decode_fp64", "rope_fp64",
+           "attention_rope_fp64", "attention_backward_fp64"]
 
 
 def _as64(x) -> np.ndarray:
@@ -295,6 +299,38 @@ def tree_decode_fp64(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, p
                 o[lo + i, h] = (p @ vs) / p.sum()
                 lse[lo + i, h] = m + np.log(p.sum())
     return o, lse
+
+
+def rope_fp64(x, cos, sin, positions=None):
+    """Rotary position embedding, float64.
+
+    "LLM study notes" (DEVOCEAN tech blog), RoPE section: each token's
+    embedding is read as complex numbers and rotated in the complex plane by
+    an angle given by the token's absolute position, so that the inner
+    product of two rotated vectors depends on their relative position only.
+    Here the complex numbers are consecutive pairs, z_i = x[2i] + j x[2i+1],
+    and row n of ``x [..., N, d]`` is rotated by the angle of position
+    ``positions[n]`` (default n): z_i -> z_i * (cos[p, i] + j sin[p, i]),
+    with ``cos``, ``sin`` of shape ``[P, d/2]``.
+    """
+    x = _as64(x)
+    n, d = x.shape[-2], x.shape[-1]
+    pos = np.arange(n) if positions is None else np.asarray(positions, dtype=np.int64)
+    c = _as64(cos)[pos]                                 # [N, d/2]
+    s = _as64(sin)[pos]
+    re, im = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = re * c - im * s
+    out[..., 1::2] = re * s + im * c
+    return out
+
+
+def attention_rope_fp64(q, k, v, cos, sin, *, causal: bool = False, scale: float | None = None,
+                        rows=None, row_block: int = 256):
+    """Attention of RoPE-rotated queries and keys (row n at position n), float64:
+    ``attention_fp64(rope(q), rope(k), v)``."""
+    return attention_fp64(rope_fp64(q, cos, sin), rope_fp64(k, cos, sin), v, causal=causal,
+                          scale=scale, rows=rows, row_block=row_block)
 
 
 def attention_backward_fp64(q, k, v, do, *, causal: bool = False, scale: float | None = None,
