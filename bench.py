@@ -14,11 +14,14 @@ the CPU oracle's rate on a bounded sample are reported in the same JSON line.
 The backward pass (fa_bwd) of both forward calls, a paged prefill
 (fa_paged_prefill: 16 sequences with 0..4096 cached tokens receiving 256..1792
 new ones, H=32, d=128, causal) and a draft-tree verification (fa_tree_decode:
-64 sequences of 128..8192 committed tokens, 64-node trees, H=32, d=128) are
-timed after the steps, each in a loop of its own, and reported under "bwd",
-"prefill" and "tree" (they are not part of the step).
+64 sequences of 128..8192 committed tokens, 64-node trees, H=32, d=128) and
+the forward with RoPE (fa_fwd_rope, query rotation fused, against fa_rope on
+q and k followed by fa_fwd) are timed after the steps, each in a loop of its
+own, and reported under "bwd", "prefill", "tree" and "rope" (they are not part
+of the step).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--skip-bwd]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--min-warmup-s 1.0]
+                    [--no-cpu-baseline] [--skip-bwd] [--skip-prefill] [--skip-tree] [--skip-rope]
 """
 from __future__ import annotations
 
@@ -158,14 +161,19 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warmup-s", type=float, default=1.0,
+                    help="after the W warmup steps, keep warming each timed section until this "
+                         "much wall time has passed (the GPU's clocks ramp up under sustained "
+                         "load; a few milliseconds of warmup measure a partly idle GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
                     help="forward only (for profiling the forward kernel alone)")
     ap.add_argument("--skip-bwd", action="store_true", help="do not time the backward pass")
     ap.add_argument("--skip-prefill", action="store_true", help="do not time the paged prefill")
     ap.add_argument("--skip-tree", action="store_true", help="do not time the tree verification")
+    ap.add_argument("--skip-rope", action="store_true", help="do not time the RoPE forward")
     ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode", "bwd-noncausal",
-                                       "bwd-causal", "prefill", "tree"],
+                                       "bwd-causal", "prefill", "tree", "rope"],
                     help="run one call per step (for per-kernel counter runs)")
     ap.add_argument("--probe-copy", type=int, metavar="MIB",
                     help="instead of the hot path, copy a buffer of MIB MiB a few times "
@@ -192,6 +200,16 @@ def main():
         print(json.dumps({"probe_copy_bytes_each_way": n * 4, "copies": max(1, args.steps)}))
         return
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+
+    def warm_up(fn):
+        """W untimed calls, then more until --min-warmup-s of wall time has passed."""
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + args.min_warmup_s
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
 
     # ---- forward inputs ----
     cfg = w.FWD_CONFIGS["fwd_b8_h16_n2048_d128"]
@@ -253,9 +271,7 @@ def main():
             acc[1] += ev[1].elapsed_time(ev[2])
             acc[2] += ev[2].elapsed_time(ev[3])
 
-    for _ in range(args.warmup):
-        step(False, None)
-    torch.cuda.synchronize()
+    warm_up(lambda: step(False, None))
     log("warmup done")
 
     # whole-step wall time (no per-call syncs inside)
@@ -333,9 +349,8 @@ def main():
         evb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for causal in bwd_modes:
             o_, lse_ = fwd_out[causal]
-            for _ in range(args.warmup):
-                fa.fa_bwd(qd, kd, vd, o_, lse_, do, dq, dk, dv, causal, cfg.scale, wsb)
-            torch.cuda.synchronize()
+            warm_up(lambda: fa.fa_bwd(qd, kd, vd, o_, lse_, do, dq, dk, dv, causal, cfg.scale,
+                                      wsb))
             tot = 0.0
             for _ in range(args.steps):
                 evb[0].record(stream)
@@ -377,9 +392,7 @@ def main():
         def pcall():
             fa.fa_paged_prefill(qp, ppools[0], ppools[1], btp, slp, cup, op_, lsep, wl.max_q_len,
                                 True, Lp.scale)
-        for _ in range(args.warmup):
-            pcall()
-        torch.cuda.synchronize()
+        warm_up(pcall)
         evp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         tot = 0.0
         for _ in range(args.steps):
@@ -422,9 +435,7 @@ def main():
         def tcall():
             fa.fa_tree_decode(qt_, tpools[0], tpools[1], btt, slt, cut, prt, ot, lset,
                               wlt.max_q_len, Lt.scale)
-        for _ in range(args.warmup):
-            tcall()
-        torch.cuda.synchronize()
+        warm_up(tcall)
         evt = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         tot = 0.0
         for _ in range(args.steps):
@@ -443,10 +454,55 @@ def main():
                        "flops": fl, "algorithmic_bytes": by}
         log("tree timed")
 
+    # ---- forward with RoPE: fused query rotation vs rotate-then-attend ----
+    t_rope = None
+    if not args.skip_rope and args.only in (None, "rope"):
+        rc, rs = (torch.from_numpy(t).to(dev) for t in w.rope_tables(cfg.N, cfg.d))
+        wsr = torch.empty(fa.fa_fwd_rope_workspace_size(cfg.B, cfg.H, cfg.N, cfg.d),
+                          dtype=torch.uint8, device=dev)
+        # the unfused path rotates k into the same workspace the fused call
+        # uses, so both read their keys from the same memory (the forward's
+        # speed depends on where its operands sit, by up to ~15%)
+        qrot = torch.empty_like(qd)
+        krot = wsr.view(torch.bfloat16).view(qd.shape)
+        orr = torch.empty_like(qd)
+        lsr = torch.empty_like(lse_nc)
+        evr = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+        def timed(fn):
+            warm_up(fn)
+            tot = 0.0
+            for _ in range(args.steps):
+                evr[0].record(stream)
+                fn()
+                evr[1].record(stream)
+                evr[1].synchronize()
+                tot += evr[0].elapsed_time(evr[1])
+            return tot / args.steps
+
+        out["rope"] = {}
+        for causal in (False, True):
+            tag = "causal" if causal else "noncausal"
+
+            def fused():
+                fa.fa_fwd_rope(qd, kd, vd, orr, lsr, rc, rs, causal, cfg.scale, wsr)
+
+            def unfused():
+                fa.fa_rope(qd, qrot, rc, rs)
+                fa.fa_rope(kd, krot, rc, rs)
+                fa.fa_fwd(qrot, krot, vd, orr, lsr, causal, cfg.scale)
+            tf_, tu_ = timed(fused), timed(unfused)
+            fl = fwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, causal)
+            out["rope"].update({f"{tag}_fused_ms": round(tf_, 4), f"{tag}_unfused_ms": round(tu_, 4),
+                                f"{tag}_fused_tflops": round(fl / (tf_ * 1e-3) / 1e12, 2)})
+            if not causal:
+                t_rope = tf_
+        log("rope timed")
+
     if args.only is not None:
         ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,
               "bwd-noncausal": t_bwd.get(False), "bwd-causal": t_bwd.get(True),
-              "prefill": t_pre, "tree": t_tree}[args.only]
+              "prefill": t_pre, "tree": t_tree, "rope": t_rope}[args.only]
         print(json.dumps({"only": args.only, "ms": ms}), flush=True)
         return
     if not args.no_cpu_baseline:

@@ -1,5 +1,5 @@
 """MI355X-native exact attention: FlashAttention-style forward and backward, paged-KV
-decode, paged prefill and draft-tree verification.
+decode, paged prefill, draft-tree verification and RoPE (standalone and fused).
 
 The compute path is hand-written HIP for gfx950 behind a C ABI (``libfa.so``,
 declared in ``include/fa.h``).  This package is the thin Python binding over
@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     FA_BF16, FA_F32, FaError, attention, attention_backward, fa_bwd, fa_bwd_workspace_size,
     fa_fwd, fa_paged_decode, fa_paged_decode_workspace_size, fa_paged_prefill, fa_status_string,
     fa_last_hip_error, fa_tree_decode, library_path, load_library, paged_decode, paged_prefill,
-    tree_decode,
+    tree_decode, fa_rope, fa_fwd_rope, fa_fwd_rope_workspace_size, rope, attention_rope,
 )

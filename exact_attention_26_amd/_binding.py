@@ -63,6 +63,14 @@ def load_library():
     lib.fa_tree_decode.argtypes = [c.c_void_p] * 9 + [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int,
                                                       c.c_int64, c.c_int, c.c_int, c.c_float,
                                                       c.c_int, c.c_void_p]
+    lib.fa_rope.restype = c.c_int
+    lib.fa_rope.argtypes = [c.c_void_p] * 4 + [c.c_int] * 5 + [c.c_void_p]
+    lib.fa_fwd_rope_workspace_size.restype = c.c_size_t
+    lib.fa_fwd_rope_workspace_size.argtypes = [c.c_int] * 4
+    lib.fa_fwd_rope.restype = c.c_int
+    lib.fa_fwd_rope.argtypes = [c.c_void_p] * 7 + [c.c_int] * 5 + [c.c_float, c.c_int,
+                                                                   c.c_void_p, c.c_size_t,
+                                                                   c.c_void_p]
     lib.fa_status_string.restype = c.c_char_p
     lib.fa_status_string.argtypes = [c.c_int]
     lib.fa_last_hip_error.restype = c.c_int
@@ -286,6 +294,60 @@ def fa_tree_decode(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, tre
         raise FaError(st, "fa_tree_decode")
 
 
+def _check_tables(rope_cos, rope_sin, N, d, device):
+    torch = _torch()
+    for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        _check_dense(name, t, device)
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] < N or t.shape[1] != d // 2:
+            raise ValueError(f"{name} must be float32 [>= N][d/2]")
+
+
+def fa_rope(x, out, rope_cos, rope_sin) -> None:
+    """Call ``fa_rope`` on ``[B][H][N][d]`` tensors (``out`` may be ``x``)."""
+    if x.dim() != 4:
+        raise ValueError("x must be [B][H][N][d]")
+    B, H, N, d = x.shape
+    _check_dense("x", x, x.device)
+    _check_dense("out", out, x.device)
+    if tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    _check_tables(rope_cos, rope_sin, N, d, x.device)
+    st = load_library().fa_rope(_ptr(x), _ptr(out), _ptr(rope_cos), _ptr(rope_sin), B, H, N, d,
+                                _dtype_code(x), _stream(x.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_rope")
+
+
+def fa_fwd_rope_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_fwd_rope_workspace_size(B, H, N, d))
+
+
+def fa_fwd_rope(q, k, v, o, lse, rope_cos, rope_sin, causal: bool, scale: float,
+                workspace) -> None:
+    """Call ``fa_fwd_rope``: ``fa_fwd`` on RoPE-rotated q and k."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][H][N][d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("workspace", workspace)):
+        _check_dense(name, t, dev)
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q's shape and dtype")
+    if lse is not None:
+        _check_dense("lse", lse, dev)
+        if tuple(lse.shape) != (B, H, N) or lse.dtype != _torch().float32:
+            raise ValueError("lse must be float32 [B][H][N]")
+    _check_tables(rope_cos, rope_sin, N, d, dev)
+    st = load_library().fa_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                    _ptr(rope_cos), _ptr(rope_sin), B, H, N, d,
+                                    int(bool(causal)), float(scale), _dtype_code(q),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(dev))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_rope")
+
+
 # --------------------------------------------------------------------------
 # convenience wrappers that allocate outputs with torch
 # --------------------------------------------------------------------------
@@ -341,6 +403,29 @@ def tree_decode(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, tree_p
     lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
     fa_tree_decode(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, tree_parents, o, lse,
                    max_q_len, scale)
+    return o, lse
+
+
+def rope(x, rope_cos, rope_sin):
+    """RoPE of ``x [B][H][N][d]`` (row n at position n).  Returns a new tensor."""
+    out = _torch().empty_like(x)
+    fa_rope(x, out, rope_cos, rope_sin)
+    return out
+
+
+def attention_rope(q, k, v, rope_cos, rope_sin, causal: bool = False, scale: float | None = None,
+                   workspace=None):
+    """Attention of RoPE-rotated q and k, query rotation fused.  Returns ``(o, lse)``."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty(max(fa_fwd_rope_workspace_size(B, H, N, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    fa_fwd_rope(q, k, v, o, lse, rope_cos, rope_sin, causal, scale, workspace)
     return o, lse
 
 

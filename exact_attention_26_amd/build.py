@@ -19,19 +19,20 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["fa_fwd.hip", "fa_fwd_bf16.hip", "fa_bwd.hip", "fa_prefill.hip", "fa_decode.hip",
-           "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_fwd_bf16.hip", "fa_bwd.hip", "fa_prefill.hip", "fa_rope.hip",
+           "fa_decode.hip", "fa_api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + INCLUDE, "-I" + CSRC]
 
 
-# Per-source extra flags.  The bf16 forward and the paged prefill (both built
-# on fwd_block) keep every MFMA accumulator in VGPRs: the whole working set
+# Per-source extra flags.  The bf16 forward, the paged prefill / tree and the
+# RoPE forward (all built on fwd_block) keep every MFMA accumulator in VGPRs: the whole working set
 # fits in 256 VGPRs at two waves per SIMD, and the softmax reads the score
 # accumulators with VALU instructions.
 EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "fa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "fa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "fa_rope.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -98,6 +98,30 @@ fa_status fa_tree_decode(const void* q, const void* k_cache, const void* v_cache
                                             static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_rope(const void* x, void* out, const float* rope_cos, const float* rope_sin, int B,
+                  int H, int N, int d, int dtype, void* stream) {
+    const fa_status st = fa_host::check_rope(x, out, rope_cos, rope_sin, B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    return hip_status(fa_launch_rope(x, out, rope_cos, rope_sin, B, H, N, d,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_fwd_rope_workspace_size(int B, int H, int N, int d) {
+    return fa_host::fwd_rope_workspace_bytes(B, H, N, d);
+}
+
+fa_status fa_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const float* rope_cos, const float* rope_sin, int B, int H, int N, int d,
+                      int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    const fa_status st = fa_host::check_fwd_rope(q, k, v, o, rope_cos, rope_sin, B, H, N, d,
+                                                 causal, scale, dtype, workspace,
+                                                 workspace_bytes);
+    if (st != FA_OK) return st;
+    return hip_status(fa_launch_fwd_rope(q, k, v, o, lse, rope_cos, rope_sin, B, H, N, d, causal,
+                                         scale, workspace, static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_string(int status) { return fa_host::status_string(status); }
 
 int fa_last_hip_error(void) { return t_last_hip_error; }

@@ -21,6 +21,10 @@
 //    register staging), double-buffered in two separate LDS arrays, one
 //    barrier per tile; rows are stored with their 16-byte chunks XOR-swizzled
 //    (swz), which makes the K reads and the transposed V reads conflict-free.
+//    The next tile's K loads go out at the top of a tile and its V loads
+//    after the score MFMAs: the K and V tiles of one index are often a large
+//    power of two apart in memory, and requesting both at once made them
+//    collide (about 15% slower when K and V sit exactly 64 MiB apart).
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
 //    Q in registers as the B operand): a lane holds one query and 16 keys, so
 //    row max / row sum are in-lane plus one v_permlane32_swap.
@@ -69,15 +73,18 @@ struct DenseKV {
         for (int i = 0; i < FwdShape<D>::LPW; ++i)
             gofs[i] = tile_load_offset<D>(wave * FwdShape<D>::LPW + i, lane);
     }
-    // Issue tile kt's loads into `stage` (K tile, then V tile).  Returns the
-    // tile's pages that must be hidden (none here).
-    __device__ __forceinline__ uint32_t load(int kt, uint16_t* stage, int wave) const {
+    // Issue tile kt's K loads into `stage`.  Returns the tile's pages that
+    // must be hidden (none here).
+    __device__ __forceinline__ uint32_t load_k(int kt, uint16_t* stage, int wave) {
         constexpr int LPW = FwdShape<D>::LPW;
-        const int bytes = len * D * 2;
-        const int tb = kt * kFwdBN * D * 2;
-        load_tile_lds<LPW>(K, bytes, tb, &gofs[0], stage, wave * LPW);
-        load_tile_lds<LPW>(V, bytes, tb, &gofs[0], stage + FwdShape<D>::TILE, wave * LPW);
+        load_tile_lds<LPW>(K, len * D * 2, kt * kFwdBN * D * 2, &gofs[0], stage, wave * LPW);
         return 0u;
+    }
+    // Issue tile kt's V loads into `stage` (after load_k of the same tile).
+    __device__ __forceinline__ void load_v(int kt, uint16_t* stage, int wave) {
+        constexpr int LPW = FwdShape<D>::LPW;
+        load_tile_lds<LPW>(V, len * D * 2, kt * kFwdBN * D * 2, &gofs[0],
+                           stage + FwdShape<D>::TILE, wave * LPW);
     }
 };
 
@@ -114,7 +121,9 @@ struct PagedKV {
         const int64_t id = table[p];
         return (id >= 0 && id < num_blocks) ? id : -1;
     }
-    __device__ __forceinline__ uint32_t load(int kt, uint16_t* stage, int wave) const {
+    int64_t cur_off = 0;                       // this wave's page of the tile being loaded
+    int cur_bytes = 0;
+    __device__ __forceinline__ uint32_t load_k(int kt, uint16_t* stage, int wave) {
         constexpr int LPW = FwdShape<D>::LPW;
         const int n_pages = (len + kPage - 1) / kPage;
         uint32_t hide = 0u;
@@ -127,11 +136,15 @@ struct PagedKV {
             if (w == wave) mine = id;
         }
         const int rows = (mine < 0) ? 0 : min(kPage, len - (4 * kt + wave) * kPage);
-        const int64_t off = (mine < 0 ? 0 : mine) * page_stride + head_off;
-        const int bytes = rows * D * 2;
-        load_tile_lds<LPW>(Kc + off, bytes, 0, &gofs[0], stage, wave * LPW);
-        load_tile_lds<LPW>(Vc + off, bytes, 0, &gofs[0], stage + FwdShape<D>::TILE, wave * LPW);
+        cur_off = (mine < 0 ? 0 : mine) * page_stride + head_off;
+        cur_bytes = rows * D * 2;
+        load_tile_lds<LPW>(Kc + cur_off, cur_bytes, 0, &gofs[0], stage, wave * LPW);
         return hide;
+    }
+    __device__ __forceinline__ void load_v(int kt, uint16_t* stage, int wave) {
+        constexpr int LPW = FwdShape<D>::LPW;
+        load_tile_lds<LPW>(Vc + cur_off, cur_bytes, 0, &gofs[0], stage + FwdShape<D>::TILE,
+                           wave * LPW);
     }
 };
 
@@ -144,6 +157,11 @@ struct QRows {
     int64_t stride;                            // elements between consecutive rows
     int64_t lse_stride;
     int rows;                                  // valid rows
+    // RoPE mode only: cosine / sine tables [positions][D/2] and the position
+    // of row 0 (row r is at position pos0 + r)
+    const float* rope_cos = nullptr;
+    const float* rope_sin = nullptr;
+    int pos0 = 0;
 };
 
 // Largest draft tree of the tree mode (one 64-bit path mask per node).
@@ -156,8 +174,9 @@ constexpr int kMaxTreeNodes = 64;
 // sees the keys before `shift` (the committed tokens) and the tree keys of
 // the nodes on its path from the root, found by walking `parents` (node r's
 // parent among the rows, or -1; parents come first).  A row that sees no key
-// gets O = 0 and LSE = -inf.
-template <int D, bool CAUSAL, class KV, bool TREE = false>
+// gets O = 0 and LSE = -inf.  ROPE: the query rows are rotated on load
+// (rotate_pairs, consecutive pairs, the angle of the row's position).
+template <int D, bool CAUSAL, class KV, bool TREE = false, bool ROPE = false>
 __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, const QRows& qr,
                                           KV& kv, int q0, int shift, float scale_log2,
                                           const int32_t* parents = nullptr) {
@@ -183,15 +202,56 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
     const uint32_t qflip = (scale_log2 < 0.f) ? 0x80008000u : 0u;   // fold a negative scale into Q
     const float tau_raw = (c > 0.f) ? kRescaleThreshold / c : __builtin_inff();
 
+    // ---- tiles: causal blocks stop at the last key their last row sees;
+    //      tiles before n_full need no mask (every key exists and is seen by
+    //      every row of the block)
+    const int n_kt_all = (N + kFwdBN - 1) / kFwdBN;
+    int n_kt = n_kt_all, n_full = N / kFwdBN;
+    if (TREE) n_full = min(n_full, max(shift, 0) / kFwdBN);   // tiles of committed tokens only
+    if (CAUSAL) {
+        const int last = shift + min(qr.rows, q0 + kFwdBM) - 1;   // last key any row sees
+        n_kt = last < 0 ? 0 : min(n_kt_all, last / kFwdBN + 1);
+        const int first = shift + q0;                             // last key the first row sees
+        n_full = first < kFwdBN - 1 ? 0 : min(n_full, (first + 1) / kFwdBN);
+    }
+    n_full = min(n_full, n_kt);
+
+    // ---- the first K/V tile's HBM -> LDS loads go out before anything else,
+    //      so their latency overlaps the query loads below
+    kv.setup(wave, lane);
+    uint32_t hide_next = 0u;                   // pages of the next tile to hide (paged)
+    if (n_kt > 0) {
+        hide_next = kv.load_k(0, smem0, wave);
+        kv.load_v(0, smem0, wave);
+    }
+
     // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
     bf16x8 qop[NKC];
+    {
+        // branch-free: rows past the end load the last row (qr.rows >= 1
+        // whenever a block runs) and are zeroed afterwards
+        const int qld = min(qrow, qr.rows - 1);
+        const uint32_t keep = (qrow < qr.rows) ? 0xFFFFFFFFu : 0u;
+        u32x4 xq[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (qrow < qr.rows)
-            x = *reinterpret_cast<const u32x4*>(qr.Q + qrow * qr.stride + kc * 16 + g * 8);
-        x ^= qflip;
-        qop[kc] = __builtin_bit_cast(bf16x8, x);
+        for (int kc = 0; kc < NKC; ++kc)
+            xq[kc] = *reinterpret_cast<const u32x4*>(qr.Q + qld * qr.stride + kc * 16 + g * 8);
+        if constexpr (ROPE) {
+            // all table loads in flight together, then the rotation: elements
+            // kc*16 + 8g .. +8 are pairs kc*8 + 4g .. +4
+            float4 cq[NKC], sq[NKC];
+            const int64_t t0 = (int64_t)(qr.pos0 + qld) * (D / 2) + g * 4;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                cq[kc] = *reinterpret_cast<const float4*>(qr.rope_cos + t0 + kc * 8);
+                sq[kc] = *reinterpret_cast<const float4*>(qr.rope_sin + t0 + kc * 8);
+            }
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) xq[kc] = rotate_pairs(xq[kc], cq[kc], sq[kc]);
+        }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+            qop[kc] = __builtin_bit_cast(bf16x8, (xq[kc] & keep) ^ qflip);
     }
 
     f32x16 oacc[ND];
@@ -217,22 +277,7 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
         }
     }
 
-    // ---- tiles: causal blocks stop at the last key their last row sees;
-    //      tiles before n_full need no mask (every key exists and is seen by
-    //      every row of the block)
-    const int n_kt_all = (N + kFwdBN - 1) / kFwdBN;
-    int n_kt = n_kt_all, n_full = N / kFwdBN;
-    if (TREE) n_full = min(n_full, max(shift, 0) / kFwdBN);   // tiles of committed tokens only
-    if (CAUSAL) {
-        const int last = shift + min(qr.rows, q0 + kFwdBM) - 1;   // last key any row sees
-        n_kt = last < 0 ? 0 : min(n_kt_all, last / kFwdBN + 1);
-        const int first = shift + q0;                             // last key the first row sees
-        n_full = first < kFwdBN - 1 ? 0 : min(n_full, (first + 1) / kFwdBN);
-    }
-    n_full = min(n_full, n_kt);
 
-    kv.setup(wave, lane);
-    uint32_t hide_next = 0u;                   // pages of the next tile to hide (paged)
 
     // ---- per-lane LDS offsets (elements) of the MFMA operand reads; the row
     //      offsets 32kb (+16cc, +8) do not change the swizzle, so they and the
@@ -257,10 +302,14 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
         const uint32_t hide = hide_next;
         __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads have landed
         __syncthreads();
-        if (kt + 1 < n_kt) hide_next = kv.load(kt + 1, nxt, wave);
+        if (kt + 1 < n_kt) hide_next = kv.load_k(kt + 1, nxt, wave);
         const int k0 = kt * kFwdBN;
-        if (wq0 >= qr.rows) return;            // no row of this wave exists
-        if (MASK && CAUSAL && k0 > shift + wq0 + 31) return;   // tile after all of this wave's keys
+        // a wave with nothing to compute here (no row of it exists, or the tile
+        // lies after all of its keys) still issues its share of the next V tile
+        if (wq0 >= qr.rows || (MASK && CAUSAL && k0 > shift + wq0 + 31)) {
+            if (kt + 1 < n_kt) kv.load_v(kt + 1, nxt, wave);
+            return;
+        }
 
         // ---- S^T = K Q^T for 2 blocks of 32 keys
         f32x16 sacc[2];
@@ -287,6 +336,7 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
+        if (kt + 1 < n_kt) kv.load_v(kt + 1, nxt, wave);   // the next tile's V, staggered
 
         // ---- online softmax; lane holds query qrow and keys
         //      k0 + 32kb + 8(r/4) + 4g + r%4 (page 2kb + r/8 of the tile)
@@ -368,7 +418,6 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
     //      diagonal); tile kt lives in stage kt & 1.
     using NoMask = std::integral_constant<bool, false>;
     using Mask = std::integral_constant<bool, true>;
-    if (n_kt > 0) hide_next = kv.load(0, smem0, wave);
     int kt = 0;
     for (; kt < n_full; kt += 2) {
         tile_step(kt, smem0, smem1, NoMask{});

@@ -151,4 +151,24 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
     return w;
 }
 
+// Rotate the four complex numbers (x[2i] + j x[2i+1], i = 0..3) held as 8
+// bf16 in x by the angles whose cosines / sines are c, s: fp32 arithmetic,
+// results rounded to nearest even bf16.
+__device__ __forceinline__ u32x4 rotate_pairs(u32x4 x, float4 c, float4 s) {
+    const float cs[4] = {c.x, c.y, c.z, c.w};
+    const float sn[4] = {s.x, s.y, s.z, s.w};
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float re = __uint_as_float(x[w] << 16);          // element 2w
+        const float im = __uint_as_float(x[w] & 0xFFFF0000u);  // element 2w + 1
+        const float nre = fmaf(re, cs[w], -im * sn[w]);
+        const float nim = fmaf(re, sn[w], im * cs[w]);
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)nre);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)nim);
+        out[w] = lo | (hi << 16);
+    }
+    return out;
+}
+
 }  // namespace fa_gfx950

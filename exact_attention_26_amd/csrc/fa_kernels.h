@@ -36,6 +36,14 @@ hipError_t fa_launch_tree_decode(const void* q, const void* k_cache, const void*
                                  int64_t num_blocks, int total_q, float scale,
                                  hipStream_t stream);
 
+// RoPE (fa_rope.hip): standalone rotation, and the forward with fused query rotation
+hipError_t fa_launch_rope(const void* x, void* out, const float* rope_cos, const float* rope_sin,
+                          int B, int H, int N, int d, hipStream_t stream);
+hipError_t fa_launch_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const float* rope_cos, const float* rope_sin, int B, int H, int N,
+                              int d, int causal, float scale, void* workspace,
+                              hipStream_t stream);
+
 hipError_t fa_launch_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   void* o, float* lse, int S, int H, int d,

@@ -151,6 +151,41 @@ inline fa_status check_tree(const void* q, const void* kc, const void* vc, const
     return FA_OK;
 }
 
+inline fa_status check_rope(const void* x, const void* out, const void* c, const void* s, int B,
+                            int H, int N, int d, int dtype) {
+    if (!x || !out || !c || !s) return FA_ERR_INVALID;
+    if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID;
+    const double elems = double(B) * H * N * d;
+    if (elems >= 4611686018427387904.0) return FA_ERR_INVALID;
+    if (elems / 8.0 / 256.0 > 2147483647.0) return FA_ERR_INVALID;      // 1-D grid
+    if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+// Forward with RoPE: the rotated keys go to the workspace, [B][H][N][d] bf16.
+inline size_t fwd_rope_workspace_bytes(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    const double bytes = double(B) * H * N * d * 2.0;
+    if (bytes > 1.0e15) return 0;
+    return size_t(B) * size_t(H) * size_t(N) * size_t(d) * 2;
+}
+
+inline fa_status check_fwd_rope(const void* q, const void* k, const void* v, const void* o,
+                                const void* c, const void* s, int B, int H, int N, int d,
+                                int causal, float scale, int dtype, const void* ws,
+                                size_t ws_bytes) {
+    if (!c || !s) return FA_ERR_INVALID;
+    fa_status st = check_fwd(q, k, v, o, B, H, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    st = check_rope(k, ws ? ws : k, c, s, B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    const size_t need = fwd_rope_workspace_bytes(B, H, N, d);
+    if (need == 0 || !ws || ws_bytes < need) return FA_ERR_INVALID;
+    return FA_OK;
+}
+
 inline const char* status_string(int s) {
     switch (s) {
         case FA_OK: return "FA_OK";

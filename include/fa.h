@@ -1,7 +1,7 @@
 /*
  * fa.h - C ABI of libfa.so: exact scaled-dot-product attention on MI355X (gfx950).
  *
- * Five operations sit behind this interface.
+ * Six operations sit behind this interface.
  *
  *   fa_fwd           the attention forward pass computed FlashAttention-style:
  *                    Q, K, V in device memory, O (and the per-row log-sum-exp)
@@ -16,6 +16,8 @@
  *                    prefill, continuous batching).
  *   fa_tree_decode   the nodes of a draft token tree per sequence attending to
  *                    that paged cache under a tree mask (speculative decoding).
+ *   fa_rope,         rotary position embedding of queries / keys, standalone and
+ *   fa_fwd_rope      fused into the forward pass.
  *
  * What is computed.  For every batch b and head h, with s_ij = scale * q_i . k_j
  * over the keys j that query i may see (all j, or j <= i when causal):
@@ -299,6 +301,64 @@ fa_status fa_tree_decode(const void* q, const void* k_cache, const void* v_cache
                          void* o, float* lse, int num_seqs, int H, int d, int page_size,
                          int max_blocks_per_seq, int64_t num_blocks, int total_q, int max_q_len,
                          float scale, int dtype, void* stream);
+
+/*
+ * fa_rope - rotary position embedding (RoPE) of a [B][H][N][d] tensor.
+ *
+ * "LLM study notes" (DEVOCEAN tech blog), RoPE section: a token's embedding is
+ * read as complex numbers and rotated in the complex plane by an angle given
+ * by its absolute position, so that the inner product of a rotated query and
+ * a rotated key depends only on their relative position.  Here the complex
+ * numbers are consecutive pairs z_i = x[2i] + j x[2i+1], and row n of every
+ * (b, h) -- position n -- becomes z_i * (cos[n][i] + j sin[n][i]), computed in
+ * fp32 and rounded to nearest-even bf16.  The tables carry any frequency
+ * schedule (the usual one turns pair i by n * 10000^(-2i/d) radians).
+ *
+ *   x          [B][H][N][d] bf16                                   (read)
+ *   out        [B][H][N][d] bf16; may be x itself (in place)      (written)
+ *   rope_cos,  [N][d/2] float32 cosine / sine of each (position,   (read)
+ *   rope_sin   pair) angle
+ *   d          64 or 128;  dtype FA_BF16
+ *
+ * Returns FA_OK, FA_ERR_INVALID (null pointer, sizes < 1), FA_ERR_UNSUPPORTED
+ * (d, dtype), or FA_ERR_HIP.
+ */
+fa_status fa_rope(const void* x, void* out, const float* rope_cos, const float* rope_sin,
+                  int B, int H, int N, int d, int dtype, void* stream);
+
+/*
+ * fa_fwd_rope_workspace_size - bytes of workspace fa_fwd_rope needs:
+ * B * H * N * d * 2 (the rotated keys).  0 if the sizes are invalid.
+ */
+size_t fa_fwd_rope_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fa_fwd_rope - fa_fwd on RoPE-rotated queries and keys, the query rotation
+ * fused into the attention kernel.
+ *
+ * Kernel fusion ("LLM study notes", kernel fusion section) saves the global
+ * memory round trip of an intermediate.  Each work group rotates its query
+ * rows once, in registers, as it loads them (the rotated queries never reach
+ * HBM).  The keys are rotated once per head into the workspace (fa_rope's
+ * kernel) before the attention kernel runs: every query block of a head
+ * reads every key tile, so rotating keys inside the attention kernel would
+ * repeat each rotation N/128 times.  The result equals fa_fwd on
+ * fa_rope(q) and fa_rope(k).
+ *
+ *   q, k       [B][H][N][d] bf16, NOT rotated; row n is at position n   (read)
+ *   v, o, lse, B, H, N, d, causal, scale, stream   as in fa_fwd (bf16 only)
+ *   rope_cos, rope_sin   as in fa_rope ([N][d/2] float32)                  (read)
+ *   workspace  device scratch of at least fa_fwd_rope_workspace_size(B, H, N, d)
+ *              bytes, owned by the caller; contents on entry do not matter;
+ *              not shared with a call running on another stream.
+ *
+ * Returns FA_OK, FA_ERR_INVALID (fa_fwd's checks, null tables, workspace NULL
+ * or too small), FA_ERR_UNSUPPORTED (d, dtype), or FA_ERR_HIP.
+ */
+fa_status fa_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const float* rope_cos, const float* rope_sin,
+                      int B, int H, int N, int d, int causal, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);

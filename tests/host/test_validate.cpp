@@ -151,6 +151,18 @@ int main() {
     EXPECT_EQ(check_tree(p, p, p, p, p, p, p, p, 64, 32, 128, 16, 520, 14707, 4096, 65, 0.088f,
                          FA_BF16), FA_ERR_UNSUPPORTED);
 
+    // rope
+    EXPECT_EQ(check_rope(p, p, p, p, 8, 16, 2048, 128, FA_BF16), FA_OK);
+    EXPECT_EQ(check_rope(p, p, nullptr, p, 8, 16, 2048, 128, FA_BF16), FA_ERR_INVALID);
+    EXPECT_EQ(check_rope(p, p, p, p, 8, 16, 2048, 96, FA_BF16), FA_ERR_UNSUPPORTED);
+    EXPECT_EQ(fwd_rope_workspace_bytes(8, 16, 2048, 128), 8ull * 16 * 2048 * 128 * 2);
+    EXPECT_EQ(check_fwd_rope(p, p, p, p, p, p, 8, 16, 2048, 128, 1, 0.088f, FA_BF16, p,
+                             fwd_rope_workspace_bytes(8, 16, 2048, 128)), FA_OK);
+    EXPECT_EQ(check_fwd_rope(p, p, p, p, p, p, 8, 16, 2048, 128, 1, 0.088f, FA_BF16, p, 100),
+              FA_ERR_INVALID);
+    EXPECT_EQ(check_fwd_rope(p, p, p, p, nullptr, p, 8, 16, 2048, 128, 1, 0.088f, FA_BF16, p,
+                             fwd_rope_workspace_bytes(8, 16, 2048, 128)), FA_ERR_INVALID);
+
     EXPECT_EQ(std::string_view(status_string(FA_OK)).size() > 0, 1);
     if (failures) {
         std::fprintf(stderr, "%d check(s) failed\n", failures);

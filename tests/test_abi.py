@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted([
         "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
         "fa_paged_decode_workspace_size", "fa_paged_prefill", "fa_status_string",
-        "fa_last_hip_error", "fa_tree_decode"])
+        "fa_last_hip_error", "fa_tree_decode", "fa_rope", "fa_fwd_rope_workspace_size",
+        "fa_fwd_rope"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -158,6 +159,34 @@ def _tree(**kw):
 ])
 def test_tree_rejects_before_launch(kw, status):
     assert _tree(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(out=None), 1), (dict(c=None), 1), (dict(s=None), 1), (dict(N=0), 1),
+    (dict(d=96), 2), (dict(dtype=fa.FA_F32), 2),
+])
+def test_rope_rejects_before_launch(kw, status):
+    a = dict(x=FAKE, out=FAKE, c=FAKE, s=FAKE, B=1, H=2, N=16, d=64, dtype=fa.FA_BF16)
+    a.update(kw)
+    assert fa.load_library().fa_rope(a["x"], a["out"], a["c"], a["s"], a["B"], a["H"], a["N"],
+                                     a["d"], a["dtype"], None) == status
+
+
+def test_fwd_rope_workspace_and_rejections():
+    lib = fa.load_library()
+    assert fa.fa_fwd_rope_workspace_size(8, 16, 2048, 128) == 8 * 16 * 2048 * 128 * 2
+    assert fa.fa_fwd_rope_workspace_size(0, 1, 1, 64) == 0
+    ws = fa.fa_fwd_rope_workspace_size(1, 1, 16, 64)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, c=FAKE, s=FAKE, N=16, d=64, dtype=fa.FA_BF16,
+                 ws=FAKE, wsb=ws)
+        a.update(kw)
+        return lib.fa_fwd_rope(a["q"], a["k"], a["v"], a["o"], None, a["c"], a["s"], 1, 1, a["N"],
+                               a["d"], 0, 0.125, a["dtype"], a["ws"], a["wsb"], None)
+    assert call(c=None) == 1 and call(s=None) == 1 and call(ws=None) == 1
+    assert call(wsb=ws - 1) == 1 and call(q=None) == 1 and call(N=0) == 1
+    assert call(d=96) == 2 and call(dtype=fa.FA_F32) == 2
 
 
 def test_host_validation_unit_with_sanitizers(tmp_path):
