@@ -110,16 +110,19 @@ def decode_bytes(layout):
 
 def measured_traffic(kernel_key: str):
     """HBM bytes per launch (read + written) from the committed counter summary
-    profiles/traffic.json, or None when the kernel source changed since."""
+    profiles/traffic.json, or None when any source the kernel is built from
+    changed since the counters were taken."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             rec = json.load(f)["kernels"][kernel_key]
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
     except (OSError, KeyError, ValueError):
         return None
-    if sha != rec["sha256_16"]:
+    if h.hexdigest()[:16] != rec["sha256_16"]:
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
@@ -201,6 +204,20 @@ def main():
         return
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
 
+    def time_calls(fn):
+        """Mean milliseconds of fn() over --steps calls, from HIP events recorded
+        on the launch stream around each call.  All calls are enqueued before
+        the one synchronisation at the end, so the GPU runs them back to back
+        and no interval contains host time spent enqueueing the next call."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
     def warm_up(fn):
         """W untimed calls, then more until --min-warmup-s of wall time has passed."""
         for _ in range(args.warmup):
@@ -248,46 +265,46 @@ def main():
         log(f"decode inputs ready: {L.num_blocks} pages, sum L = {int(L.seq_lens.sum())}")
 
     stream = torch.cuda.current_stream(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
     run_nc = args.only in (None, "fwd-noncausal", "bwd-noncausal")
     run_c = args.only in (None, "fwd-causal", "bwd-causal")
     run_dec = decode and args.only in (None, "decode")
 
-    def step(timed, acc):
-        ev[0].record(stream)
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
         if run_nc:
             fa.fa_fwd(qd, kd, vd, o_nc, lse_nc, False, cfg.scale)
-        ev[1].record(stream)
+        if ev is not None:
+            ev[1].record(stream)
         if run_c:
             fa.fa_fwd(qd, kd, vd, o_c, lse_c, True, cfg.scale)
-        ev[2].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
         if run_dec:
             fa.fa_paged_decode(qdec, kc, vc, bt, sl, o_dec, lse_dec, L.scale, ws)
-        ev[3].record(stream)
-        if timed:
-            ev[3].synchronize()
-            acc[0] += ev[0].elapsed_time(ev[1])
-            acc[1] += ev[1].elapsed_time(ev[2])
-            acc[2] += ev[2].elapsed_time(ev[3])
+        if ev is not None:
+            ev[3].record(stream)
 
-    warm_up(lambda: step(False, None))
+    warm_up(step)
     log("warmup done")
 
     # whole-step wall time (no per-call syncs inside)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(False, None)
+        step()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # per-call kernel times from HIP events on the launch stream
-    acc = [0.0, 0.0, 0.0]
-    for _ in range(args.steps):
-        step(True, acc)
+    # per-call kernel times from HIP events on the launch stream: every step's
+    # events are enqueued with it and read after one final synchronisation
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for ev in evs:
+        step(ev)
     torch.cuda.synchronize()
-    t_nc, t_c, t_dec = (a / args.steps for a in acc)
+    t_nc, t_c, t_dec = (sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / args.steps
+                        for i in range(3))
     log("timed steps done")
 
     f_nc = fwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, False)
@@ -346,19 +363,12 @@ def main():
                           device=dev)
         dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
         fwd_out = {False: (o_nc, lse_nc), True: (o_c, lse_c)}
-        evb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for causal in bwd_modes:
             o_, lse_ = fwd_out[causal]
             warm_up(lambda: fa.fa_bwd(qd, kd, vd, o_, lse_, do, dq, dk, dv, causal, cfg.scale,
                                       wsb))
-            tot = 0.0
-            for _ in range(args.steps):
-                evb[0].record(stream)
-                fa.fa_bwd(qd, kd, vd, o_, lse_, do, dq, dk, dv, causal, cfg.scale, wsb)
-                evb[1].record(stream)
-                evb[1].synchronize()
-                tot += evb[0].elapsed_time(evb[1])
-            t_bwd[causal] = tot / args.steps
+            t_bwd[causal] = time_calls(
+                lambda: fa.fa_bwd(qd, kd, vd, o_, lse_, do, dq, dk, dv, causal, cfg.scale, wsb))
         log("backward timed")
         out["bwd"] = {}
         for causal in bwd_modes:
@@ -367,6 +377,8 @@ def main():
             out["bwd"].update({f"{tag}_ms": round(t_bwd[causal], 4), f"{tag}_tflops": round(tf, 2),
                                f"{tag}_frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         out["bwd"]["flops"] = "2.5x forward (10 N^2 d per head non-causal)"
+        out["bwd"]["traffic"] = {k: measured_traffic(f"{k} B=8 H=16 N=2048") for k in (
+            "bwd_dkdv_kernel<128,false>", "bwd_dq_kernel<128,false>", "bwd_prep_kernel<128>")}
 
     # ---- paged prefill, its own timed loop ----
     t_pre = None
@@ -393,21 +405,14 @@ def main():
             fa.fa_paged_prefill(qp, ppools[0], ppools[1], btp, slp, cup, op_, lsep, wl.max_q_len,
                                 True, Lp.scale)
         warm_up(pcall)
-        evp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        tot = 0.0
-        for _ in range(args.steps):
-            evp[0].record(stream)
-            pcall()
-            evp[1].record(stream)
-            evp[1].synchronize()
-            tot += evp[0].elapsed_time(evp[1])
-        t_pre = tot / args.steps
+        t_pre = time_calls(pcall)
         fl = prefill_flops(wl, True)
         tf = fl / (t_pre * 1e-3) / 1e12
         out["prefill"] = {"ms": round(t_pre, 4), "tflops": round(tf, 2),
                           "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "causal": True,
                           "new_tokens": wl.total_q, "cached_tokens": int(Lp.seq_lens.sum()),
-                          "flops": fl}
+                          "flops": fl,
+                          "traffic": measured_traffic("prefill_bf16_kernel<128,true> P1")}
         log("prefill timed")
 
     # ---- draft-tree verification, its own timed loop ----
@@ -436,22 +441,15 @@ def main():
             fa.fa_tree_decode(qt_, tpools[0], tpools[1], btt, slt, cut, prt, ot, lset,
                               wlt.max_q_len, Lt.scale)
         warm_up(tcall)
-        evt = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        tot = 0.0
-        for _ in range(args.steps):
-            evt[0].record(stream)
-            tcall()
-            evt[1].record(stream)
-            evt[1].synchronize()
-            tot += evt[0].elapsed_time(evt[1])
-        t_tree = tot / args.steps
+        t_tree = time_calls(tcall)
         fl, by = tree_work(wlt, part)
         out["tree"] = {"ms": round(t_tree, 4),
                        "tflops": round(fl / (t_tree * 1e-3) / 1e12, 2),
                        "hbm_gbs": round(by / (t_tree * 1e-3) / 1e9, 1),
                        "hbm_frac_peak": round(by / (t_tree * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                        "nodes": wlt.total_q, "committed_tokens": int(Lt.seq_lens.sum()) - wlt.total_q,
-                       "flops": fl, "algorithmic_bytes": by}
+                       "flops": fl, "algorithmic_bytes": by,
+                       "traffic": measured_traffic("tree_bf16_kernel<128> T1")}
         log("tree timed")
 
     # ---- forward with RoPE: fused query rotation vs rotate-then-attend ----
@@ -467,18 +465,9 @@ def main():
         krot = wsr.view(torch.bfloat16).view(qd.shape)
         orr = torch.empty_like(qd)
         lsr = torch.empty_like(lse_nc)
-        evr = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-
         def timed(fn):
             warm_up(fn)
-            tot = 0.0
-            for _ in range(args.steps):
-                evr[0].record(stream)
-                fn()
-                evr[1].record(stream)
-                evr[1].synchronize()
-                tot += evr[0].elapsed_time(evr[1])
-            return tot / args.steps
+            return time_calls(fn)
 
         out["rope"] = {}
         for causal in (False, True):
