@@ -6,8 +6,10 @@
 // section), with the tiled online softmax of "Flash Attention" (velog
 // @myungum, section 2).  Work is split over batch, heads and blocks of 128
 // query rows; every work group owns its rows of O ("FlashAttention-2 GPU work
-// partitioning", iPLEX blog, section 3).  The block itself is fwd_block
-// (fa_fwd_block.h) over a dense K/V source.
+// partitioning", iPLEX blog, section 3).  Under the causal mask a work group
+// takes two blocks, a long one and a short one (causal_groups), so that all
+// work groups carry about the same number of key tiles.  The block itself is
+// fwd_block (fa_fwd_block.h) over a dense K/V source.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,9 +36,10 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int nwg = gridDim.x;
     int wg = blockIdx.x;
     if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    const int bh = wg / n_qblocks;
-    int qb = wg - bh * n_qblocks;
-    if (CAUSAL) qb = n_qblocks - 1 - qb;       // longest rows first
+    // causal: work group p of a head takes query blocks n_qblocks-1-p and p
+    const int per_head = CAUSAL ? causal_groups(n_qblocks) : n_qblocks;
+    const int bh = wg / per_head;
+    const int p = wg - bh * per_head;
     const size_t base = (size_t)bh * (size_t)N * D;
 
     DenseKV<D> kv;
@@ -50,14 +53,25 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     qr.stride = D;
     qr.lse_stride = 1;
     qr.rows = N;
-    fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, qb * kFwdBM, 0, scale_log2);
+    if (!CAUSAL) {
+        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, p * kFwdBM, 0, scale_log2);
+        return;
+    }
+    const int qb_heavy = n_qblocks - 1 - p;
+    const int n_blocks = (p < qb_heavy) ? 2 : 1;
+    for (int i = 0; i < n_blocks; ++i) {
+        if (i > 0) __syncthreads();            // the first block's last tile is read
+        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, (i == 0 ? qb_heavy : p) * kFwdBM, 0,
+                             scale_log2);
+    }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int N, float scale, hipStream_t stream) {
     const int n_qblocks = (N + kFwdBM - 1) / kFwdBM;
-    const unsigned nwg = (unsigned)B * (unsigned)H * (unsigned)n_qblocks;
+    const int per_head = CAUSAL ? causal_groups(n_qblocks) : n_qblocks;
+    const unsigned nwg = (unsigned)B * (unsigned)H * (unsigned)per_head;
     const uint16_t* qp = static_cast<const uint16_t*>(q);
     const uint16_t* kp = static_cast<const uint16_t*>(k);
     const uint16_t* vp = static_cast<const uint16_t*>(v);

@@ -148,6 +148,12 @@ struct PagedKV {
     }
 };
 
+// Causal work balance: under the causal mask query block b of n sees about
+// b + 1 key tiles, so work group p of a (sequence, head) takes blocks n-1-p
+// and p (one block when they coincide); every work group then sees about the
+// same number of tiles and no long block is left for the end of the grid.
+__host__ __device__ constexpr int causal_groups(int n_qblocks) { return (n_qblocks + 1) / 2; }
+
 // Query rows of the block: row r (0-based in the sequence / head) at
 // Q + r * stride; O the same; LSE at lse + r * lse_stride (lse may be null).
 struct QRows {

@@ -57,9 +57,9 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int nwg = gridDim.x;
     int wg = blockIdx.x;
     if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    const int bh = wg / n_qblocks;
-    int qb = wg - bh * n_qblocks;
-    if (CAUSAL) qb = n_qblocks - 1 - qb;
+    const int per_head = CAUSAL ? causal_groups(n_qblocks) : n_qblocks;
+    const int bh = wg / per_head;
+    const int p = wg - bh * per_head;
     const size_t base = (size_t)bh * (size_t)N * D;
 
     DenseKV<D> kv;
@@ -76,8 +76,14 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     qr.rope_cos = rope_cos;
     qr.rope_sin = rope_sin;
     qr.pos0 = 0;
-    fwd_block<D, CAUSAL, DenseKV<D>, false, true>(smem0, smem1, qr, kv, qb * kFwdBM, 0,
-                                                  scale_log2);
+    // causal: the blocks n_qblocks-1-p and p (causal_groups)
+    const int qb_first = CAUSAL ? n_qblocks - 1 - p : p;
+    const int n_blocks = (CAUSAL && p < qb_first) ? 2 : 1;
+    for (int i = 0; i < n_blocks; ++i) {
+        if (i > 0) __syncthreads();            // the first block's last tile is read
+        fwd_block<D, CAUSAL, DenseKV<D>, false, true>(
+            smem0, smem1, qr, kv, (i == 0 ? qb_first : p) * kFwdBM, 0, scale_log2);
+    }
 }
 
 template <int D>
@@ -96,7 +102,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       const float* c, const float* s, int B, int H, int N, float scale,
                       hipStream_t stream) {
     const int n_qblocks = (N + kFwdBM - 1) / kFwdBM;
-    const unsigned nwg = (unsigned)B * (unsigned)H * (unsigned)n_qblocks;
+    const int per_head = CAUSAL ? causal_groups(n_qblocks) : n_qblocks;
+    const unsigned nwg = (unsigned)B * (unsigned)H * (unsigned)per_head;
     const uint16_t* qp = static_cast<const uint16_t*>(q);
     const uint16_t* kp = static_cast<const uint16_t*>(k);
     const uint16_t* vp = static_cast<const uint16_t*>(v);
