@@ -18,10 +18,15 @@ new ones, H=32, d=128, causal) and a draft-tree verification (fa_tree_decode:
 the forward with RoPE (fa_fwd_rope, query rotation fused, against fa_rope on
 q and k followed by fa_fwd) are timed after the steps, each in a loop of its
 own, and reported under "bwd", "prefill", "tree" and "rope" (they are not part
-of the step).
+of the step).  As context for the MFMA fractions, "mfma_ceiling" gives what a
+plain 8192^3 bf16 GEMM through the vendor BLAS (torch.matmul) reaches on the
+same GPU in the same run (under sustained matrix load the chip runs below the
+clock its published peak assumes), and "hbm_ceiling" what a plain 2 GiB device
+copy reaches against the published HBM bandwidth.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--min-warmup-s 1.0]
                     [--no-cpu-baseline] [--skip-bwd] [--skip-prefill] [--skip-tree] [--skip-rope]
+                    [--skip-gemm]
 """
 from __future__ import annotations
 
@@ -175,6 +180,9 @@ def main():
     ap.add_argument("--skip-prefill", action="store_true", help="do not time the paged prefill")
     ap.add_argument("--skip-tree", action="store_true", help="do not time the tree verification")
     ap.add_argument("--skip-rope", action="store_true", help="do not time the RoPE forward")
+    ap.add_argument("--skip-gemm", action="store_true",
+                    help="do not time the plain bf16 GEMM (the MFMA throughput the vendor BLAS "
+                         "reaches on this GPU, reported next to the attention figures)")
     ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode", "bwd-noncausal",
                                        "bwd-causal", "prefill", "tree", "rope"],
                     help="run one call per step (for per-kernel counter runs)")
@@ -487,6 +495,41 @@ def main():
             if not causal:
                 t_rope = tf_
         log("rope timed")
+
+    # ---- context: the MFMA throughput a plain bf16 GEMM reaches through the
+    #      vendor BLAS (torch.matmul -> hipBLASLt) on the same GPU, same clocks
+    if not args.skip_gemm and args.only is None:
+        n = 8192
+        ga = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+        gb = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+        gc = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+        gemm = lambda: torch.matmul(ga, gb, out=gc)  # noqa: E731
+        warm_up(gemm)
+        t_g = time_calls(gemm)
+        tg = 2.0 * n ** 3 / (t_g * 1e-3) / 1e12
+        out["mfma_ceiling"] = {
+            "kind": "bf16 GEMM 8192x8192x8192 (torch.matmul, vendor BLAS), N(0,1) operands",
+            "ms": round(t_g, 4), "tflops": round(tg, 2),
+            "frac_peak": round(tg / PEAK_BF16_TFLOPS, 4),
+            "fwd_noncausal_over_gemm": round(tflops_nc / tg, 4) if run_nc else None,
+            "fwd_causal_over_gemm": round(tflops_c / tg, 4) if run_c else None}
+        del ga, gb, gc
+        log("gemm timed")
+        # and the HBM bandwidth of plain device copies (read + write) through
+        # torch, for the decode's GB/s
+        nb = 2 ** 31
+        src = torch.empty(nb // 2, dtype=torch.bfloat16, device=dev).normal_()
+        dst = torch.empty_like(src)
+        cp = lambda: dst.copy_(src)  # noqa: E731
+        warm_up(cp)
+        t_cp = time_calls(cp)
+        gbs_cp = 2.0 * nb / (t_cp * 1e-3) / 1e9
+        out["hbm_ceiling"] = {
+            "kind": "device copy of 2 GiB (torch copy_), read + write bytes",
+            "ms": round(t_cp, 4), "gbs": round(gbs_cp, 1),
+            "frac_peak": round(gbs_cp / PEAK_HBM_GBS, 4)}
+        del src, dst
+        log("copy timed")
 
     if args.only is not None:
         ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,
