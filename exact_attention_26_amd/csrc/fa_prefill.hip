@@ -28,20 +28,25 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                          const uint16_t* __restrict__ Vc, const int32_t* __restrict__ table,
                          const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
                          uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int max_blocks,
-                         int64_t num_blocks, int total_q, int n_qblocks, float scale_log2) {
+                         int64_t num_blocks, int total_q, int n_qblocks, int n_units,
+                         float scale_log2) {
     __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * FwdShape<D>::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
 
-    // work group -> (sequence, head, query block), query blocks of a
-    // (sequence, head) adjacent and kept on one XCD; causal: longest rows first
-    const int nwg = gridDim.x;
-    int wg = blockIdx.x;
-    if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    const int per_seq = n_qblocks * H;
-    const int s = wg / per_seq;
-    const int rem = wg - s * per_seq;
-    const int h = rem / n_qblocks;
-    int qb = rem - h * n_qblocks;
+    // work group -> (sequence, head, query block).  Work groups are dealt to
+    // the 8 XCDs round-robin (XCD = blockIdx % 8).  Unit u = (sequence u / H,
+    // head u % H) goes to XCD u % 8, its query blocks one after another there
+    // (they share the unit's K/V through that XCD's L2); so every XCD gets
+    // the same share of every sequence, however unequal the sequences are.
+    // Causal: longest rows first.
+    const int x = blockIdx.x & 7;
+    const int k = blockIdx.x >> 3;             // k-th work group on XCD x
+    const int j = k / n_qblocks;
+    const int u = 8 * j + x;
+    if (u >= n_units) return;                  // padding of the grid
+    const int s = u / H;
+    const int h = u - s * H;
+    int qb = k - j * n_qblocks;
     if (CAUSAL) qb = n_qblocks - 1 - qb;
 
     // this sequence's new rows, kept inside [0, total_q)
@@ -89,11 +94,11 @@ void tree_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * FwdShape<D>::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
 
-    const int nwg = gridDim.x;
-    int wg = blockIdx.x;
-    if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    const int s = wg / H;
-    const int h = wg - s * H;
+    // plain order: consecutive work groups (consecutive heads of a sequence)
+    // go to different XCDs, so every XCD gets the same share of every
+    // sequence; nothing is reused across work groups that an L2 could keep
+    const int s = blockIdx.x / H;
+    const int h = blockIdx.x - s * H;
 
     const int qbeg = cu_q[s];
     int rows = cu_q[s + 1] - qbeg;
@@ -128,14 +133,16 @@ hipError_t launch(const void* q, const void* k_cache, const void* v_cache, const
                   int max_blocks, int64_t num_blocks, int total_q, int max_q_len, float scale,
                   hipStream_t stream) {
     const int n_qblocks = (max_q_len + kFwdBM - 1) / kFwdBM;
-    const unsigned nwg = (unsigned)S * (unsigned)H * (unsigned)n_qblocks;
+    int n_units = S * H;                       // (sequence, head) pairs, dealt to 8 XCDs
+    const unsigned nwg = (unsigned)((n_units + 7) / 8) * 8u * (unsigned)n_qblocks;
     const uint16_t* qp = static_cast<const uint16_t*>(q);
     const uint16_t* kp = static_cast<const uint16_t*>(k_cache);
     const uint16_t* vp = static_cast<const uint16_t*>(v_cache);
     uint16_t* op = static_cast<uint16_t*>(o);
     float scale_log2 = (float)((double)scale * 1.4426950408889634074);
     void* args[] = {&qp, &kp, &vp, (void*)&table, (void*)&seq_lens, (void*)&cu_q, &op, &lse,
-                    &H, &max_blocks, &num_blocks, &total_q, (void*)&n_qblocks, &scale_log2};
+                    &H, &max_blocks, &num_blocks, &total_q, (void*)&n_qblocks, &n_units,
+                    &scale_log2};
     return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_bf16_kernel<D, CAUSAL>),
                            dim3(nwg), dim3(kFwdThreads), args, 0, stream);
 }
