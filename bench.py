@@ -22,11 +22,14 @@ of the step).  As context for the MFMA fractions, "mfma_ceiling" gives what a
 plain 8192^3 bf16 GEMM through the vendor BLAS (torch.matmul) reaches on the
 same GPU in the same run (under sustained matrix load the chip runs below the
 clock its published peak assumes), and "hbm_ceiling" what a plain 2 GiB device
-copy reaches against the published HBM bandwidth.
+copy reaches against the published HBM bandwidth.  "sweep" times the forward
+on the other configurations: the sequence sweep at 16k tokens (N = 512 ..
+16384, H=32, d=64, both masks) and the long-context one (B=1 H=16 N=16384
+d=128, causal).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--min-warmup-s 1.0]
                     [--no-cpu-baseline] [--skip-bwd] [--skip-prefill] [--skip-tree] [--skip-rope]
-                    [--skip-gemm]
+                    [--skip-sweep] [--skip-gemm]
 """
 from __future__ import annotations
 
@@ -180,6 +183,9 @@ def main():
     ap.add_argument("--skip-prefill", action="store_true", help="do not time the paged prefill")
     ap.add_argument("--skip-tree", action="store_true", help="do not time the tree verification")
     ap.add_argument("--skip-rope", action="store_true", help="do not time the RoPE forward")
+    ap.add_argument("--skip-sweep", action="store_true",
+                    help="do not time the forward over the sequence sweep (d=64) and the "
+                         "long-context configuration")
     ap.add_argument("--skip-gemm", action="store_true",
                     help="do not time the plain bf16 GEMM (the MFMA throughput the vendor BLAS "
                          "reaches on this GPU, reported next to the attention figures)")
@@ -495,6 +501,35 @@ def main():
             if not causal:
                 t_rope = tf_
         log("rope timed")
+
+    # ---- the other forward configurations: the sequence sweep at 16k tokens
+    #      (H=32, d=64) and the long-context one (B=1 H=16 N=16384 d=128,
+    #      causal, q and k with standard deviation 3), inputs drawn on the GPU
+    if not args.skip_sweep and args.only is None:
+        gen = torch.Generator(device=dev)
+        out["sweep"] = {}
+        for name, c in w.FWD_CONFIGS.items():
+            if not (name.startswith("sweep_") or name.startswith("long_")):
+                continue
+            gen.manual_seed(c.seed)
+            shape = (c.B, c.H, c.N, c.d)
+            qs = (torch.randn(shape, generator=gen, device=dev) * c.sigma_qk).to(torch.bfloat16)
+            ks = (torch.randn(shape, generator=gen, device=dev) * c.sigma_qk).to(torch.bfloat16)
+            vs = (torch.randn(shape, generator=gen, device=dev) * c.sigma_v).to(torch.bfloat16)
+            os_ = torch.empty_like(qs)
+            ls = torch.empty(shape[:-1], dtype=torch.float32, device=dev)
+            row = {}
+            for causal in c.causal:
+                fn = lambda: fa.fa_fwd(qs, ks, vs, os_, ls, causal, c.scale)  # noqa: E731
+                warm_up(fn)
+                t = time_calls(fn)
+                tag = "causal" if causal else "noncausal"
+                tf = fwd_flops(c.B, c.H, c.N, c.d, causal) / (t * 1e-3) / 1e12
+                row[f"{tag}_ms"] = round(t, 4)
+                row[f"{tag}_tflops"] = round(tf, 2)
+            out["sweep"][f"B={c.B} H={c.H} N={c.N} d={c.d}"] = row
+            del qs, ks, vs, os_, ls
+        log("sweep timed")
 
     # ---- context: the MFMA throughput a plain bf16 GEMM reaches through the
     #      vendor BLAS (torch.matmul -> hipBLASLt) on the same GPU, same clocks
