@@ -124,8 +124,10 @@ inline fa_status check_prefill(const void* q, const void* kc, const void* vc, co
     if (double(total_q) * H * d >= 4611686018427387904.0) return FA_ERR_INVALID;
     if (double(S) * max_blocks >= 2147483647.0) return FA_ERR_INVALID;   // int32 table index
     if (double(max_blocks) * page_size >= 2147483647.0) return FA_ERR_INVALID;
-    // one work group per (sequence, head, block of kFwdBlockM new rows)
-    const double groups = double(S) * H * std::ceil(double(max_q_len) / kFwdBlockM);
+    // one work group per (sequence, head, block of kFwdBlockM new rows), the
+    // (sequence, head) count padded to a multiple of 8 (the XCD dealing)
+    const double units = std::ceil(double(S) * H / 8.0) * 8.0;
+    const double groups = units * std::ceil(double(max_q_len) / kFwdBlockM);
     if (groups > 2147483647.0) return FA_ERR_INVALID;
     if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;

@@ -135,6 +135,11 @@ int main() {
                             FA_BF16), FA_ERR_INVALID);
     EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 64, 16, 1, 1, 1, 1, 0, nan, FA_BF16),
               FA_ERR_INVALID);
+    // prefill: the grid counts the (sequence, head) pairs padded to a multiple of 8
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 2147483640, 1, 64, 16, 1, 1, 1, 1, 0, 1.f,
+                            FA_BF16), FA_OK);
+    EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 2147483641, 1, 64, 16, 1, 1, 1, 1, 0, 1.f,
+                            FA_BF16), FA_ERR_INVALID);
     // prefill: unsupported
     EXPECT_EQ(check_prefill(p, p, p, p, p, p, p, 1, 1, 96, 16, 1, 1, 1, 1, 0, 1.f, FA_BF16),
               FA_ERR_UNSUPPORTED);
