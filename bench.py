@@ -317,8 +317,9 @@ def main():
     for ev in evs:
         step(ev)
     torch.cuda.synchronize()
-    t_nc, t_c, t_dec = (sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / args.steps
-                        for i in range(3))
+    per_call = [[ev[i].elapsed_time(ev[i + 1]) for ev in evs] for i in range(3)]
+    t_nc, t_c, t_dec = (sum(x) / args.steps for x in per_call)
+    med_min = [(round(float(np.median(x)), 4), round(min(x), 4)) for x in per_call]
     log("timed steps done")
 
     f_nc = fwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, False)
@@ -347,8 +348,10 @@ def main():
                    "parallelism": "single GPU"},
         "fwd": {"noncausal_ms": round(t_nc, 4), "noncausal_tflops": round(tflops_nc, 2),
                 "noncausal_frac_peak": round(tflops_nc / PEAK_BF16_TFLOPS, 4),
+                "noncausal_ms_median_min": med_min[0] if run_nc else None,
                 "causal_ms": round(t_c, 4), "causal_tflops": round(tflops_c, 2),
-                "causal_frac_peak": round(tflops_c / PEAK_BF16_TFLOPS, 4)},
+                "causal_frac_peak": round(tflops_c / PEAK_BF16_TFLOPS, 4),
+                "causal_ms_median_min": med_min[1] if run_c else None},
         "roofline": {"bound": "mfma", "achieved": round(tflops_nc, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops_nc / PEAK_BF16_TFLOPS, 4),
@@ -358,7 +361,8 @@ def main():
     }
     if decode:
         gbs = dec_bytes / (t_dec * 1e-3) / 1e9
-        out["decode"] = {"ms": round(t_dec, 4), "hbm_gbs": round(gbs, 1),
+        out["decode"] = {"ms": round(t_dec, 4), "ms_median_min": med_min[2],
+                         "hbm_gbs": round(gbs, 1),
                          "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes": dec_bytes, "logical_bytes": dec_logical,
                          "logical_gbs": round(dec_logical / (t_dec * 1e-3) / 1e9, 1)}
