@@ -190,7 +190,7 @@ def main():
                     help="do not time the plain bf16 GEMM (the MFMA throughput the vendor BLAS "
                          "reaches on this GPU, reported next to the attention figures)")
     ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode", "bwd-noncausal",
-                                       "bwd-causal", "prefill", "tree", "rope"],
+                                       "bwd-causal", "prefill", "tree", "rope", "gemm"],
                     help="run one call per step (for per-kernel counter runs)")
     ap.add_argument("--probe-copy", type=int, metavar="MIB",
                     help="instead of the hot path, copy a buffer of MIB MiB a few times "
@@ -324,9 +324,10 @@ def main():
 
     f_nc = fwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, False)
     f_c = fwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, True)
-    tflops_nc = f_nc / (t_nc * 1e-3) / 1e12
-    tflops_c = f_c / (t_c * 1e-3) / 1e12
-    value = (f_nc + f_c) / ((t_nc + t_c) * 1e-3) / 1e12
+    # (in --only modes without a forward the intervals are empty)
+    tflops_nc = f_nc / (t_nc * 1e-3) / 1e12 if t_nc > 0 else 0.0
+    tflops_c = f_c / (t_c * 1e-3) / 1e12 if t_c > 0 else 0.0
+    value = (f_nc + f_c) / ((t_nc + t_c) * 1e-3) / 1e12 if t_nc + t_c > 0 else 0.0
 
     out = {
         "metric": METRIC,
@@ -537,14 +538,15 @@ def main():
 
     # ---- context: the MFMA throughput a plain bf16 GEMM reaches through the
     #      vendor BLAS (torch.matmul -> hipBLASLt) on the same GPU, same clocks
-    if not args.skip_gemm and args.only is None:
+    t_gemm = None
+    if not args.skip_gemm and args.only in (None, "gemm"):
         n = 8192
         ga = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
         gb = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
         gc = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
         gemm = lambda: torch.matmul(ga, gb, out=gc)  # noqa: E731
         warm_up(gemm)
-        t_g = time_calls(gemm)
+        t_g = t_gemm = time_calls(gemm)
         tg = 2.0 * n ** 3 / (t_g * 1e-3) / 1e12
         out["mfma_ceiling"] = {
             "kind": "bf16 GEMM 8192x8192x8192 (torch.matmul, vendor BLAS), N(0,1) operands",
@@ -554,6 +556,7 @@ def main():
             "fwd_causal_over_gemm": round(tflops_c / tg, 4) if run_c else None}
         del ga, gb, gc
         log("gemm timed")
+    if not args.skip_gemm and args.only is None:
         # and the HBM bandwidth of plain device copies (read + write) through
         # torch, for the decode's GB/s
         nb = 2 ** 31
@@ -573,7 +576,7 @@ def main():
     if args.only is not None:
         ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,
               "bwd-noncausal": t_bwd.get(False), "bwd-causal": t_bwd.get(True),
-              "prefill": t_pre, "tree": t_tree, "rope": t_rope}[args.only]
+              "prefill": t_pre, "tree": t_tree, "rope": t_rope, "gemm": t_gemm}[args.only]
         print(json.dumps({"only": args.only, "ms": ms}), flush=True)
         return
     if not args.no_cpu_baseline:
