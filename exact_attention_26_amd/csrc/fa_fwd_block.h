@@ -1,9 +1,10 @@
 // fa_fwd_block.h - the bf16 attention forward of one block of 128 query rows
 // against one head's keys, for gfx950.  Used by the dense forward
 // (fa_fwd_bf16.hip), the paged prefill and the draft-tree verification
-// (fa_prefill.hip); they differ only in where the query rows and the K/V
-// tiles live, which a "K/V source" (DenseKV, PagedKV) and a few row pointers
-// describe, and in the mask (none, causal, tree).
+// (fa_prefill.hip) and the forward with rotary embeddings (fa_rope.hip); they
+// differ only in where the query rows and the K/V tiles live, which a "K/V
+// source" (DenseKV, PagedKV) and a few row pointers describe, in the mask
+// (none, causal, tree) and in whether the query rows are rotated on load.
 //
 // Per block: O = softmax(scale * Q K^T) V over the keys each query may see and
 // the natural-log log-sum-exp of every row, with the tiled online softmax of
