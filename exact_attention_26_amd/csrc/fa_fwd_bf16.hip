@@ -21,7 +21,7 @@ namespace {
 using namespace fa_gfx950;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2)
+__global__ __launch_bounds__(64 * dense_fwd_waves<CAUSAL>(), 8 / dense_fwd_waves<CAUSAL>())
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, int N, int n_qblocks, float scale_log2) {
@@ -42,7 +42,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int p = wg - bh * per_head;
     const size_t base = (size_t)bh * (size_t)N * D;
 
-    DenseKV<D> kv;
+    constexpr int W = dense_fwd_waves<CAUSAL>();
+    constexpr int BM = 32 * W;                 // query rows per block
+    DenseKV<D, W> kv;
     kv.K = K + base;
     kv.V = V + base;
     kv.len = N;
@@ -54,14 +56,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     qr.lse_stride = 1;
     qr.rows = N;
     if (!CAUSAL) {
-        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, p * kFwdBM, 0, scale_log2);
+        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, p * BM, 0, scale_log2);
         return;
     }
     const int qb_heavy = n_qblocks - 1 - p;
     const int n_blocks = (p < qb_heavy) ? 2 : 1;
     for (int i = 0; i < n_blocks; ++i) {
         if (i > 0) __syncthreads();            // the first block's last tile is read
-        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, (i == 0 ? qb_heavy : p) * kFwdBM, 0,
+        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, (i == 0 ? qb_heavy : p) * BM, 0,
                              scale_log2);
     }
 }
@@ -69,7 +71,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int N, float scale, hipStream_t stream) {
-    const int n_qblocks = (N + kFwdBM - 1) / kFwdBM;
+    constexpr int W = dense_fwd_waves<CAUSAL>();
+    const int n_qblocks = (N + 32 * W - 1) / (32 * W);
     const int per_head = CAUSAL ? causal_groups(n_qblocks) : n_qblocks;
     const unsigned nwg = (unsigned)B * (unsigned)H * (unsigned)per_head;
     const uint16_t* qp = static_cast<const uint16_t*>(q);
@@ -79,7 +82,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     float scale_log2 = (float)((double)scale * 1.4426950408889634074);
     void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qblocks, &scale_log2};
     return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, CAUSAL>),
-                           dim3(nwg), dim3(kFwdThreads), args, 0, stream);
+                           dim3(nwg), dim3(64 * W), args, 0, stream);
 }
 
 }  // namespace

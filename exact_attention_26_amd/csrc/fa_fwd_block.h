@@ -51,39 +51,41 @@ constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr int kFwdBM = kFwdWaves * 32;         // query rows per work group
 constexpr float kRescaleThreshold = 8.0f;      // log2 units
 
-template <int D>
+template <int D, int W = kFwdWaves>
 struct FwdShape {
     static constexpr int TILE = kFwdBN * D;                       // elements per K or V tile
-    static constexpr int LPW = TILE * 2 / 1024 / kFwdWaves;       // 1 KiB loads per wave per tensor
+    static constexpr int LPW = TILE * 2 / 1024 / W;               // 1 KiB loads per wave per tensor
     static constexpr int NKC = D / 16;                            // S^T MFMAs along d
     static constexpr int ND = D / 32;                             // 32-row blocks of O^T
 };
 
-// K/V of one head stored densely, [rows][D]; tile kt = rows 64kt .. 64kt+63.
-// Buffer resources span the head, so rows past the end arrive as zeros.
-template <int D>
+// K/V of one head stored densely, [rows][D]; tile kt = rows 64kt .. 64kt+63,
+// loaded by the W waves of the work group.  Buffer resources span the head,
+// so rows past the end arrive as zeros.
+template <int D, int W = kFwdWaves>
 struct DenseKV {
     static constexpr bool kPaged = false;
+    static constexpr int kWaves = W;
     const uint16_t* K;
     const uint16_t* V;
     int len;                                   // keys
-    int gofs[FwdShape<D>::LPW];                // this lane's byte offset in the tile, per load
+    int gofs[FwdShape<D, W>::LPW];             // this lane's byte offset in the tile, per load
 
     __device__ __forceinline__ void setup(int wave, int lane) {
 #pragma unroll
-        for (int i = 0; i < FwdShape<D>::LPW; ++i)
-            gofs[i] = tile_load_offset<D>(wave * FwdShape<D>::LPW + i, lane);
+        for (int i = 0; i < FwdShape<D, W>::LPW; ++i)
+            gofs[i] = tile_load_offset<D>(wave * FwdShape<D, W>::LPW + i, lane);
     }
     // Issue tile kt's K loads into `stage`.  Returns the tile's pages that
     // must be hidden (none here).
     __device__ __forceinline__ uint32_t load_k(int kt, uint16_t* stage, int wave) {
-        constexpr int LPW = FwdShape<D>::LPW;
+        constexpr int LPW = FwdShape<D, W>::LPW;
         load_tile_lds<LPW>(K, len * D * 2, kt * kFwdBN * D * 2, &gofs[0], stage, wave * LPW);
         return 0u;
     }
     // Issue tile kt's V loads into `stage` (after load_k of the same tile).
     __device__ __forceinline__ void load_v(int kt, uint16_t* stage, int wave) {
-        constexpr int LPW = FwdShape<D>::LPW;
+        constexpr int LPW = FwdShape<D, W>::LPW;
         load_tile_lds<LPW>(V, len * D * 2, kt * kFwdBN * D * 2, &gofs[0],
                            stage + FwdShape<D>::TILE, wave * LPW);
     }
@@ -99,6 +101,7 @@ struct DenseKV {
 template <int D>
 struct PagedKV {
     static constexpr bool kPaged = true;
+    static constexpr int kWaves = kFwdWaves;   // one page of a tile per wave
     static constexpr int kPage = 16;
     const uint16_t* Kc;
     const uint16_t* Vc;
@@ -149,6 +152,14 @@ struct PagedKV {
     }
 };
 
+// Waves per work group of the dense forwards: 8 without the mask (256 query
+// rows share every K/V tile in LDS: half the HBM -> LDS traffic per flop, one
+// work group per CU; measured about 2 % faster than 4), 4 under the causal
+// mask (two work groups per CU; with 256-row blocks the diagonal tiles and
+// the balance of the grid cost more than the shared tiles save).
+template <bool CAUSAL>
+__host__ __device__ constexpr int dense_fwd_waves() { return CAUSAL ? 4 : 8; }
+
 // Causal work balance: under the causal mask query block b of n sees about
 // b + 1 key tiles, so work group p of a (sequence, head) takes blocks n-1-p
 // and p (one block when they coincide); every work group then sees about the
@@ -174,7 +185,8 @@ struct QRows {
 // Largest draft tree of the tree mode (one 64-bit path mask per node).
 constexpr int kMaxTreeNodes = 64;
 
-// One block of kFwdBM query rows starting at row q0.  Causal: row r sees the
+// One block of 32 x KV::kWaves query rows (one wave per 32 rows) starting at
+// row q0.  Causal: row r sees the
 // keys 0 .. shift + r (shift = 0 for square attention; for new tokens at the
 // end of a sequence of kv.len tokens, shift = kv.len - rows).  TREE: the rows
 // are the nodes of a draft tree whose K/V are the last `rows` keys; row r
@@ -216,7 +228,7 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
     int n_kt = n_kt_all, n_full = N / kFwdBN;
     if (TREE) n_full = min(n_full, max(shift, 0) / kFwdBN);   // tiles of committed tokens only
     if (CAUSAL) {
-        const int last = shift + min(qr.rows, q0 + kFwdBM) - 1;   // last key any row sees
+        const int last = shift + min(qr.rows, q0 + 32 * KV::kWaves) - 1;   // last key any row sees
         n_kt = last < 0 ? 0 : min(n_kt_all, last / kFwdBN + 1);
         const int first = shift + q0;                             // last key the first row sees
         n_full = first < kFwdBN - 1 ? 0 : min(n_full, (first + 1) / kFwdBN);

@@ -46,7 +46,7 @@ void rope_kernel(const uint16_t* x, uint16_t* y, const float* __restrict__ rope_
 
 // The dense forward with the query rotation fused (K already rotated).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2)
+__global__ __launch_bounds__(64 * dense_fwd_waves<CAUSAL>(), 8 / dense_fwd_waves<CAUSAL>())
 void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, const float* __restrict__ rope_cos,
@@ -62,7 +62,9 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int p = wg - bh * per_head;
     const size_t base = (size_t)bh * (size_t)N * D;
 
-    DenseKV<D> kv;
+    constexpr int W = dense_fwd_waves<CAUSAL>();
+    constexpr int BM = 32 * W;                 // query rows per block
+    DenseKV<D, W> kv;
     kv.K = K + base;
     kv.V = V + base;
     kv.len = N;
@@ -81,8 +83,8 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int n_blocks = (CAUSAL && p < qb_first) ? 2 : 1;
     for (int i = 0; i < n_blocks; ++i) {
         if (i > 0) __syncthreads();            // the first block's last tile is read
-        fwd_block<D, CAUSAL, DenseKV<D>, false, true>(
-            smem0, smem1, qr, kv, (i == 0 ? qb_first : p) * kFwdBM, 0, scale_log2);
+        fwd_block<D, CAUSAL, DenseKV<D, W>, false, true>(
+            smem0, smem1, qr, kv, (i == 0 ? qb_first : p) * BM, 0, scale_log2);
     }
 }
 
@@ -101,7 +103,8 @@ template <int D, bool CAUSAL>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       const float* c, const float* s, int B, int H, int N, float scale,
                       hipStream_t stream) {
-    const int n_qblocks = (N + kFwdBM - 1) / kFwdBM;
+    constexpr int W = dense_fwd_waves<CAUSAL>();
+    const int n_qblocks = (N + 32 * W - 1) / (32 * W);
     const int per_head = CAUSAL ? causal_groups(n_qblocks) : n_qblocks;
     const unsigned nwg = (unsigned)B * (unsigned)H * (unsigned)per_head;
     const uint16_t* qp = static_cast<const uint16_t*>(q);
@@ -112,7 +115,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
     void* args[] = {&qp, &kp, &vp, &op, &lse, (void*)&c, (void*)&s, &N, (void*)&n_qblocks,
                     &scale_log2};
     return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_rope_bf16_kernel<D, CAUSAL>),
-                           dim3(nwg), dim3(kFwdThreads), args, 0, stream);
+                           dim3(nwg), dim3(64 * W), args, 0, stream);
 }
 
 }  // namespace
