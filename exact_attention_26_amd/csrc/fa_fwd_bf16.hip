@@ -4,12 +4,13 @@
 // and the natural-log log-sum-exp of every row, exactly as defined for scaled
 // dot-product attention ("LLM study notes", DEVOCEAN tech blog, self-attention
 // section), with the tiled online softmax of "Flash Attention" (velog
-// @myungum, section 2).  Work is split over batch, heads and blocks of 128
-// query rows; every work group owns its rows of O ("FlashAttention-2 GPU work
-// partitioning", iPLEX blog, section 3).  Under the causal mask a work group
-// takes two blocks, a long one and a short one (causal_groups), so that all
-// work groups carry about the same number of key tiles.  The block itself is
-// fwd_block (fa_fwd_block.h) over a dense K/V source.
+// @myungum, section 2).  Work is split over batch, heads and blocks of 256
+// query rows (128 under the causal mask, dense_fwd_waves); every work group
+// owns its rows of O ("FlashAttention-2 GPU work partitioning", iPLEX blog,
+// section 3).  Under the causal mask a work group takes two blocks, a long
+// one and a short one (causal_groups), so that all work groups carry about
+// the same number of key tiles.  The block itself is fwd_block
+// (fa_fwd_block.h) over a dense K/V source.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -15,9 +15,9 @@
 // partitioning", iPLEX blog, section 3).
 //
 // gfx950 mapping
-//  * 4 waves x 32 query rows.  All of a wave's state fits in 256 VGPRs, so
-//    two work groups share a CU and one wave's softmax overlaps the other's
-//    MFMAs.
+//  * 32 query rows per wave, 4 or 8 waves per work group (the K/V source's
+//    kWaves).  All of a wave's state fits in 256 VGPRs, so two waves share
+//    each SIMD and one wave's softmax overlaps the other's MFMAs.
 //  * K and V tiles (64 keys) go HBM -> LDS with buffer_load ... lds (no
 //    register staging), double-buffered in two separate LDS arrays, one
 //    barrier per tile; rows are stored with their 16-byte chunks XOR-swizzled
