@@ -26,8 +26,10 @@ def to_host(t) -> np.ndarray:
 
 
 def sample_rows(N: int, rng, extra: int = 40) -> np.ndarray:
-    """Rows at tile edges (64 and 128), the middle, the end, plus random ones."""
-    fixed = [0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, N // 2 - 1, N // 2, N - 2, N - 1]
+    """Rows at wave and block edges (32, 64, 128, 256), the middle, the end,
+    plus random ones."""
+    fixed = [0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, 255, 256, 257,
+             N // 2 - 1, N // 2, N - 2, N - 1]
     rows = np.concatenate([np.array(fixed), rng.choice(N, size=min(extra, N), replace=False)])
     return np.unique(np.clip(rows, 0, N - 1))
 

@@ -122,6 +122,28 @@ def test_full_size_sampled_rows(gpu_device, name):
         del o, lse
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_sampled_rows(gpu_device, causal):
+    """N = 32768 keys (512 key tiles; 128 blocks of 256 rows without the mask,
+    256 blocks of 128 paired into 128 work groups with it), a ragged N too;
+    oracle on sampled rows."""
+    import torch
+    for n in (32768, 32768 - 77):
+        q, k, v = w.fwd_inputs(1, 2, n, 128, seed=81 + n)
+        qd, kd, vd = (to_dev(x, "bf16", gpu_device) for x in (q, k, v))
+        say(f"fwd long B=1 H=2 N={n} d=128 causal={causal}")
+        o, lse = fa.attention(qd, kd, vd, causal=causal)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(n)
+        for h in range(2):
+            rows = sample_rows(n, rng, extra=24)
+            ro, rl = attention_fp64(q[0, h], k[0, h], v[0, h], causal=causal,
+                                    scale=1 / math.sqrt(128), rows=rows)
+            assert_close(f"o N={n} h={h}", to_host(o[0, h, rows]), ro, O_ATOL["bf16"])
+            assert_close(f"lse N={n} h={h}", to_host(lse[0, h, rows]), rl, LSE_ATOL["bf16"])
+        del o, lse, qd, kd, vd
+
+
 def test_deterministic(gpu_device):
     import torch
     q, k, v = w.fwd_inputs(2, 4, 777, 128, seed=61)
