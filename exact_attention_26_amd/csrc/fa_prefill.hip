@@ -77,6 +77,34 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, q0, L - rows, scale_log2);
 }
 
+// Batches of up to this many sequences are verified longest first.
+constexpr int kSortedSeqs = kFwdThreads;
+
+// The sequence of rank t among the S <= kSortedSeqs sequences ordered by
+// decreasing cached length (ties: lower index first), computed by every work
+// group for itself: thread i reads sequence i's length and counts the
+// sequences ahead of it.  Called by all threads of the group.
+__device__ __forceinline__ int seq_by_length_rank(const int32_t* __restrict__ seq_lens, int S,
+                                                  int max_len, int t, int* len_sh, int* pick) {
+    const int i = threadIdx.x;
+    int len = 0;
+    if (i < S) {
+        len = max(0, min(seq_lens[i], max_len));
+        len_sh[i] = len;
+    }
+    __syncthreads();
+    if (i < S) {
+        int rank = 0;
+        for (int j = 0; j < S; ++j) {
+            const int v = len_sh[j];
+            rank += (v > len || (v == len && j < i)) ? 1 : 0;
+        }
+        if (rank == t) *pick = i;
+    }
+    __syncthreads();
+    return *pick;
+}
+
 // Draft-tree verification ("LLM study notes", speculative decoding section:
 // the target model computes every node of the draft tree in one pass with
 // tree attention): the rows of sequence s are the nodes of its draft tree,
@@ -94,11 +122,21 @@ void tree_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * FwdShape<D>::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
 
-    // plain order: consecutive work groups (consecutive heads of a sequence)
-    // go to different XCDs, so every XCD gets the same share of every
-    // sequence; nothing is reused across work groups that an L2 could keep
-    const int s = blockIdx.x / H;
-    const int h = blockIdx.x - s * H;
+    __shared__ int len_sh[kSortedSeqs];
+    __shared__ int pick;
+
+    // consecutive work groups (the heads of one sequence) go to different
+    // XCDs, so every XCD gets the same share of every sequence (nothing is
+    // reused across work groups that an L2 could keep), and the sequences
+    // come longest first (up to kSortedSeqs of them), so that no long one is
+    // left for the end of the grid
+    const int n_seq = gridDim.x / H;
+    const int t = blockIdx.x / H;
+    const int h = blockIdx.x - t * H;
+    const int s = (n_seq <= kSortedSeqs)
+                      ? seq_by_length_rank(seq_lens, n_seq, max_blocks * PagedKV<D>::kPage, t,
+                                           len_sh, &pick)
+                      : t;
 
     const int qbeg = cu_q[s];
     int rows = cu_q[s + 1] - qbeg;
