@@ -24,14 +24,14 @@ def _upload(layout, q, kc, vc, device):
             torch.from_numpy(layout.seq_lens).to(device))
 
 
-def _decode(layout, q, kc, vc, device, seq_lens=None, table=None):
+def _decode(layout, q, kc, vc, device, seq_lens=None, table=None, scale=None):
     import torch
     qd, kd, vd, bt, sl = _upload(layout, q, kc, vc, device)
     if seq_lens is not None:
         sl = torch.from_numpy(np.asarray(seq_lens, np.int32)).to(device)
     if table is not None:
         bt = torch.from_numpy(np.asarray(table, np.int32)).to(device)
-    o, lse = fa.paged_decode(qd, kd, vd, bt, sl, scale=layout.scale)
+    o, lse = fa.paged_decode(qd, kd, vd, bt, sl, scale=layout.scale if scale is None else scale)
     torch.cuda.synchronize()
     return to_host(o), to_host(lse)
 
@@ -54,6 +54,18 @@ def test_edge_lengths(gpu_device, d):
     ro, rl = paged_decode_fp64(q, kc, vc, L.block_table, L.seq_lens, scale=L.scale)
     assert_close("o", o, ro, O_ATOL["bf16"])
     assert_close("lse", lse, rl, LSE_ATOL["bf16"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_negative_and_zero_scale(gpu_device, d):
+    lens = [1, 17, 300, 1025]
+    L, q, kc, vc = _small_layout(83, lens, d=d, H=2)
+    for scale in (-0.2, 0.0):
+        say(f"decode d={d} scale={scale}")
+        o, lse = _decode(L, q, kc, vc, gpu_device, scale=scale)
+        ro, rl = paged_decode_fp64(q, kc, vc, L.block_table, L.seq_lens, scale=scale)
+        assert_close(f"o scale={scale}", o, ro, O_ATOL["bf16"])
+        assert_close(f"lse scale={scale}", lse, rl, LSE_ATOL["bf16"])
 
 
 def test_empty_and_clamped_and_bad_pages(gpu_device):

@@ -78,6 +78,20 @@ def test_scale_is_applied(gpu_device):
         assert_close("lse", lse, rl, LSE_ATOL["bf16"])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_negative_scale(gpu_device, d):
+    # softmax(scale * s) with scale < 0 favours the smallest scores; the sign
+    # has to reach the scores, not only the exponent's factor
+    q, k, v = w.fwd_inputs(1, 2, 333, d, seed=43 + d)
+    for dtype in ("bf16", "f32"):
+        for causal in (False, True):
+            say(f"fwd {dtype} d={d} N=333 scale=-0.2 causal={causal}")
+            o, lse = _run(q, k, v, dtype, causal, -0.2, gpu_device)
+            ro, rl = attention_fp64(q, k, v, causal=causal, scale=-0.2)
+            assert_close(f"o {dtype} causal={causal}", o, ro, O_ATOL[dtype])
+            assert_close(f"lse {dtype} causal={causal}", lse, rl, LSE_ATOL[dtype])
+
+
 def test_huge_logit_shift(gpu_device):
     # a common offset of about +-100 on every score of a row: exp() overflows
     # (or underflows to an all-zero row) unless the running maximum is subtracted

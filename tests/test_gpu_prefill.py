@@ -18,9 +18,10 @@ def _pools(wl, poison=True):
     return kc, vc
 
 
-def _run(wl, q, kc, vc, causal, device, table=None, seq_lens=None, max_q_len=None):
+def _run(wl, q, kc, vc, causal, device, table=None, seq_lens=None, max_q_len=None, scale=None):
     import torch
     L = wl.layout
+    scale = L.scale if scale is None else scale
     table = L.block_table if table is None else table
     seq_lens = L.seq_lens if seq_lens is None else seq_lens
     o, lse = fa.paged_prefill(to_dev(q, "bf16", device), to_dev(kc, "bf16", device),
@@ -28,7 +29,7 @@ def _run(wl, q, kc, vc, causal, device, table=None, seq_lens=None, max_q_len=Non
                               torch.from_numpy(np.ascontiguousarray(table)).to(device),
                               torch.from_numpy(np.ascontiguousarray(seq_lens)).to(device),
                               torch.from_numpy(wl.cu_seqlens_q).to(device),
-                              max_q_len or wl.max_q_len, causal=causal, scale=L.scale)
+                              max_q_len or wl.max_q_len, causal=causal, scale=scale)
     torch.cuda.synchronize()
     return to_host(o), to_host(lse)
 
@@ -79,6 +80,20 @@ def test_prefill_short_and_empty_sequences(gpu_device, causal):
                               causal=causal, scale=L.scale)
     assert np.isinf(want[1]).any()
     _check(f"short causal={causal}", got, want)
+
+
+def test_prefill_negative_scale(gpu_device):
+    wl = w.prefill_workload(615, S=3, H=2, d=128, ctx_lens=[0, 70, 300], new_lens=[45, 130, 9],
+                            spare=4)
+    q = w.prefill_q(wl)
+    kc, vc = _pools(wl)
+    L = wl.layout
+    for causal in (True, False):
+        say(f"prefill scale=-0.2 causal={causal}")
+        got = _run(wl, q, kc, vc, causal, gpu_device, scale=-0.2)
+        want = paged_prefill_fp64(q, kc, vc, L.block_table, L.seq_lens, wl.cu_seqlens_q,
+                                  causal=causal, scale=-0.2)
+        _check(f"negative scale causal={causal}", got, want)
 
 
 def test_prefill_unresolvable_page_is_not_seen(gpu_device):

@@ -94,6 +94,18 @@ def test_fwd_rope_edges(gpu_device, d, causal):
         _check_fused(f"N={n}", q, k, v, c, s, causal, 1 / math.sqrt(d), to_host(o), to_host(lse))
 
 
+def test_fwd_rope_negative_scale(gpu_device):
+    n, d = 300, 128
+    q, k, v = w.fwd_inputs(1, 2, n, d, seed=931)
+    c, s, cd, sd = _tables(n, d, gpu_device)
+    for causal in (False, True):
+        say(f"fwd_rope N={n} d={d} scale=-0.2 causal={causal}")
+        o, lse = fa.attention_rope(*(to_dev(x, "bf16", gpu_device) for x in (q, k, v)), cd, sd,
+                                   causal=causal, scale=-0.2)
+        _check_fused(f"scale=-0.2 causal={causal}", q, k, v, c, s, causal, -0.2, to_host(o),
+                     to_host(lse))
+
+
 def test_fwd_rope_full_size_and_matches_unfused(gpu_device):
     """The forward bench workload (B=8 H=16 N=2048 d=128) with RoPE: sampled
     rows against the oracle; and the fused call gives the same bits as

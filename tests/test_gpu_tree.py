@@ -10,14 +10,15 @@ from oracle import tree_decode_fp64
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, parents, q, kc, vc, device, max_q_len=None):
+def _run(wl, parents, q, kc, vc, device, max_q_len=None, scale=None):
     import torch
     L = wl.layout
+    scale = L.scale if scale is None else scale
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(device)  # noqa: E731
     o, lse = fa.tree_decode(to_dev(q, "bf16", device), to_dev(kc, "bf16", device),
                             to_dev(vc, "bf16", device), t(L.block_table), t(L.seq_lens),
                             t(wl.cu_seqlens_q), t(parents.astype(np.int32)),
-                            max_q_len or wl.max_q_len, scale=L.scale)
+                            max_q_len or wl.max_q_len, scale=scale)
     torch.cuda.synchronize()
     return to_host(o), to_host(lse)
 
@@ -78,6 +79,20 @@ def test_tree_parents_out_of_range_are_roots(gpu_device):
     want = tree_decode_fp64(q, kc, vc, L.block_table, L.seq_lens, wl.cu_seqlens_q, parents,
                             scale=L.scale)
     _check("bad parents", got, want)
+
+
+def test_tree_negative_scale(gpu_device):
+    wl, _ = w.tree_workload(715, S=2, H=2, d=128, ctx_lens=[0, 90], new_lens=[7, 30], spare=4)
+    parents = np.array([-1, 0, 0, 1, -1, 4, 2] + [-1] + list(range(29)), dtype=np.int32)
+    q = w.prefill_q(wl)
+    kc = w.decode_pool(wl.layout, "k", poison=True)
+    vc = w.decode_pool(wl.layout, "v", poison=True)
+    L = wl.layout
+    say("tree scale=-0.2")
+    got = _run(wl, parents, q, kc, vc, gpu_device, scale=-0.2)
+    want = tree_decode_fp64(q, kc, vc, L.block_table, L.seq_lens, wl.cu_seqlens_q, parents,
+                            scale=-0.2)
+    _check("negative scale", got, want)
 
 
 def test_tree_full_size(gpu_device):
