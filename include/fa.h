@@ -185,7 +185,8 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int page_size,
  *   o            [S][H][d] elements of `dtype`              (written)
  *   lse          [S][H] float32 natural-log log-sum-exp, or NULL
  *   num_seqs (S), H >= 1 (each at most 65535);  d: 64 or 128 (else FA_ERR_UNSUPPORTED);
- *   page_size: 16 (else FA_ERR_UNSUPPORTED);  max_blocks_per_seq >= 1;
+ *   page_size: 16 (else FA_ERR_UNSUPPORTED);  max_blocks_per_seq >= 1, with
+ *   ceil(max_blocks_per_seq / 32) * H <= 2^31 - 1 (one work group per 32 pages and head);
  *   num_blocks >= 1;  scale finite;  dtype: FA_BF16 (FA_F32 -> UNSUPPORTED)
  *   workspace    device scratch of at least
  *                fa_paged_decode_workspace_size(S, H, d, page_size, max_blocks_per_seq)
@@ -201,8 +202,9 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int page_size,
  *   table entries past page ceil(seq_lens[s]/page_size)-1, and cache slots
  *   past seq_lens[s] in the last page, are never read.
  *
- * Returns FA_OK, FA_ERR_INVALID (null required pointer, sizes < 1, non-finite
- * scale, workspace NULL or too small), FA_ERR_UNSUPPORTED, or FA_ERR_HIP.
+ * Returns FA_OK, FA_ERR_INVALID (null required pointer, sizes < 1 or past the
+ * limits above, non-finite scale, workspace NULL or too small),
+ * FA_ERR_UNSUPPORTED, or FA_ERR_HIP.
  */
 fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, const int32_t* seq_lens,

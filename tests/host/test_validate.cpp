@@ -78,6 +78,13 @@ int main() {
               FA_ERR_INVALID);
     EXPECT_EQ(check_decode(p, p, p, p, p, p, 0, 32, 128, 16, 512, 17874, 0.1f, FA_BF16, p, ws),
               FA_ERR_INVALID);
+    // decode: the grid's x dimension holds ceil(max_blocks / 32) * H work groups
+    EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65535, 64, 16, 32768 * 32, 17874, 0.1f, FA_BF16,
+                           p, SIZE_MAX), FA_OK);                       // 2147450880 groups
+    EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65535, 64, 16, 32768 * 32 + 1, 17874, 0.1f,
+                           FA_BF16, p, SIZE_MAX), FA_ERR_INVALID);     // 2147516415 groups
+    EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65536, 64, 16, 512, 17874, 0.1f, FA_BF16, p,
+                           SIZE_MAX), FA_ERR_INVALID);
     // decode: unsupported
     EXPECT_EQ(check_decode(p, p, p, p, p, p, 64, 32, 128, 8, 512, 17874, 0.1f, FA_BF16, p, ws),
               FA_ERR_UNSUPPORTED);
