@@ -97,8 +97,11 @@ struct DenseKV {
 // Slots past the sequence's length are never read (the buffer resource of a
 // page ends at its last valid row: the rest arrives as zeros), and a table
 // entry outside [0, num_blocks) is not followed: the page arrives as zeros
-// and the caller hides its keys.
-template <int D>
+// and the caller hides its keys.  STREAM: the pages are read by this work
+// group only (one block of query rows per sequence and head), so the loads
+// are non-temporal; with several query blocks per sequence they are not (the
+// blocks re-read the same pages through L2).
+template <int D, bool STREAM = false>
 struct PagedKV {
     static constexpr bool kPaged = true;
     static constexpr int kWaves = kFwdWaves;   // one page of a tile per wave
@@ -142,12 +145,12 @@ struct PagedKV {
         const int rows = (mine < 0) ? 0 : min(kPage, len - (4 * kt + wave) * kPage);
         cur_off = (mine < 0 ? 0 : mine) * page_stride + head_off;
         cur_bytes = rows * D * 2;
-        load_tile_lds<LPW>(Kc + cur_off, cur_bytes, 0, &gofs[0], stage, wave * LPW);
+        load_tile_lds<LPW, STREAM ? kLoadNT : 0>(Kc + cur_off, cur_bytes, 0, &gofs[0], stage, wave * LPW);
         return hide;
     }
     __device__ __forceinline__ void load_v(int kt, uint16_t* stage, int wave) {
         constexpr int LPW = FwdShape<D>::LPW;
-        load_tile_lds<LPW>(Vc + cur_off, cur_bytes, 0, &gofs[0], stage + FwdShape<D>::TILE,
+        load_tile_lds<LPW, STREAM ? kLoadNT : 0>(Vc + cur_off, cur_bytes, 0, &gofs[0], stage + FwdShape<D>::TILE,
                            wave * LPW);
     }
 };

@@ -67,11 +67,15 @@ __device__ __forceinline__ int tile_load_offset(int region, int lane) {
     return (row * D + swz<D>(row, lane % CPR) * 8) * 2;
 }
 
+// Cache policy of a buffer load: non-temporal (data read once per launch).
+constexpr int kLoadNT = 2;
+
 // Rows [tbase/(2D), +TILE_ROWS) of a [rows][D] bf16 matrix X (rows*D*2 = bytes)
 // into LDS `dst`, swizzled: this wave issues NLOAD 1 KiB loads, regions
 // first_region .. first_region+NLOAD-1, with gofs[i] = tile_load_offset of its
 // region.  The buffer resource spans X, so rows past its end arrive as zeros.
-template <int NLOAD>
+// AUX: cache policy of the loads (0, or kLoadNT).
+template <int NLOAD, int AUX = 0>
 __device__ __forceinline__ void load_tile_lds(const uint16_t* X, int bytes, int tbase,
                                               const int* gofs, uint16_t* dst, int first_region) {
     const __amdgpu_buffer_rsrc_t rs =
@@ -79,7 +83,7 @@ __device__ __forceinline__ void load_tile_lds(const uint16_t* X, int bytes, int 
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (first_region + i) * 512), 16,
-                                                 gofs[i], tbase, 0, 0);
+                                                 gofs[i], tbase, 0, AUX);
 }
 
 // One 1 KiB block of x (bytes [offset, offset + 1024) of a buffer of `bytes`

@@ -145,7 +145,8 @@ void tree_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     if (rows == 0) return;
     const int L = max(0, min(seq_lens[s], max_blocks * PagedKV<D>::kPage));
 
-    PagedKV<D> kv;
+    // one work group reads this (sequence, head)'s pages: streaming loads
+    PagedKV<D, true> kv;
     kv.Kc = Kc;
     kv.Vc = Vc;
     kv.table = table + (size_t)s * max_blocks;
@@ -161,8 +162,8 @@ void tree_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     qr.lse_stride = H;
     qr.rows = rows;
     // the tree's K/V are the last `rows` of the L cached tokens
-    fwd_block<D, false, PagedKV<D>, true>(smem0, smem1, qr, kv, 0, L - rows, scale_log2,
-                                          parents + qbeg);
+    fwd_block<D, false, PagedKV<D, true>, true>(smem0, smem1, qr, kv, 0, L - rows, scale_log2,
+                                                parents + qbeg);
 }
 
 template <int D, bool CAUSAL>
