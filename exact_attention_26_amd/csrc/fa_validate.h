@@ -96,9 +96,10 @@ inline fa_status check_decode(const void* q, const void* kc, const void* vc, con
     if (S < 1 || H < 1 || d < 1 || page_size < 1 || max_blocks < 1 || num_blocks < 1)
         return FA_ERR_INVALID;
     if (!std::isfinite(scale)) return FA_ERR_INVALID;
-    if (S > 65535 || H > 65535) return FA_ERR_INVALID;                   // grid y limit
-    // one work group per (chunk of pages, head) in the grid's x dimension
-    if (double(decode_max_splits(max_blocks)) * H > 2147483647.0) return FA_ERR_INVALID;
+    if (S > 65535 || H > 65535) return FA_ERR_INVALID;
+    // grid: x = (sequence, head) pairs, y = chunks of 32 pages
+    if (double(S) * H > 2147483647.0) return FA_ERR_INVALID;
+    if (decode_max_splits(max_blocks) > 65535) return FA_ERR_INVALID;
     const double pool = double(num_blocks) * H * page_size * d;
     if (pool >= 4611686018427387904.0) return FA_ERR_INVALID;
     if (double(S) * max_blocks >= 2147483647.0) return FA_ERR_INVALID;   // int32 table index

@@ -184,9 +184,9 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int H, int d, int page_size,
  *   seq_lens     [S] int32, tokens cached per sequence       (read)
  *   o            [S][H][d] elements of `dtype`              (written)
  *   lse          [S][H] float32 natural-log log-sum-exp, or NULL
- *   num_seqs (S), H >= 1 (each at most 65535);  d: 64 or 128 (else FA_ERR_UNSUPPORTED);
- *   page_size: 16 (else FA_ERR_UNSUPPORTED);  max_blocks_per_seq >= 1, with
- *   ceil(max_blocks_per_seq / 32) * H <= 2^31 - 1 (one work group per 32 pages and head);
+ *   num_seqs (S), H >= 1 (each at most 65535, S * H at most 2^31 - 1);
+ *   d: 64 or 128 (else FA_ERR_UNSUPPORTED);  page_size: 16 (else FA_ERR_UNSUPPORTED);
+ *   max_blocks_per_seq >= 1 and at most 65535 * 32 (one work group per 32 pages and head);
  *   num_blocks >= 1;  scale finite;  dtype: FA_BF16 (FA_F32 -> UNSUPPORTED)
  *   workspace    device scratch of at least
  *                fa_paged_decode_workspace_size(S, H, d, page_size, max_blocks_per_seq)

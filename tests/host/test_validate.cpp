@@ -78,11 +78,15 @@ int main() {
               FA_ERR_INVALID);
     EXPECT_EQ(check_decode(p, p, p, p, p, p, 0, 32, 128, 16, 512, 17874, 0.1f, FA_BF16, p, ws),
               FA_ERR_INVALID);
-    // decode: the grid's x dimension holds ceil(max_blocks / 32) * H work groups
-    EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65535, 64, 16, 32768 * 32, 17874, 0.1f, FA_BF16,
-                           p, SIZE_MAX), FA_OK);                       // 2147450880 groups
-    EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65535, 64, 16, 32768 * 32 + 1, 17874, 0.1f,
-                           FA_BF16, p, SIZE_MAX), FA_ERR_INVALID);     // 2147516415 groups
+    // decode grid: x = S * H (sequence, head) pairs, y = ceil(max_blocks / 32) chunks
+    EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65535, 64, 16, 65535 * 32, 17874, 0.1f, FA_BF16,
+                           p, SIZE_MAX), FA_OK);                       // 65535 chunks
+    EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65535, 64, 16, 65535 * 32 + 1, 17874, 0.1f,
+                           FA_BF16, p, SIZE_MAX), FA_ERR_INVALID);     // 65536 chunks
+    EXPECT_EQ(check_decode(p, p, p, p, p, p, 65535, 32768, 64, 16, 1, 17874, 0.1f, FA_BF16, p,
+                           SIZE_MAX), FA_OK);                          // 2147450880 pairs
+    EXPECT_EQ(check_decode(p, p, p, p, p, p, 65535, 32769, 64, 16, 1, 17874, 0.1f, FA_BF16, p,
+                           SIZE_MAX), FA_ERR_INVALID);                 // 2147516415 pairs
     EXPECT_EQ(check_decode(p, p, p, p, p, p, 1, 65536, 64, 16, 512, 17874, 0.1f, FA_BF16, p,
                            SIZE_MAX), FA_ERR_INVALID);
     // decode: unsupported
