@@ -21,8 +21,10 @@ own, and reported under "bwd", "prefill", "tree" and "rope" (they are not part
 of the step).  As context for the MFMA fractions, "mfma_ceiling" gives what a
 plain 8192^3 bf16 GEMM through the vendor BLAS (torch.matmul) reaches on the
 same GPU in the same run (under sustained matrix load the chip runs below the
-clock its published peak assumes), and "hbm_ceiling" what a plain 2 GiB device
-copy reaches against the published HBM bandwidth.  "sweep" times the forward
+clock its published peak assumes), "hbm_ceiling" what a plain 2 GiB device
+copy reaches against the published HBM bandwidth, and "hbm_read_ceiling" what a
+read-only probe (libfa_probe.so) reaches sequentially and over 4 KiB chunks in
+random order, the grain of the paged kernels' reads.  "sweep" times the forward
 on the other configurations: the sequence sweep at 16k tokens (N = 512 ..
 16384, H=32, d=64, both masks) and the long-context one (B=1 H=16 N=16384
 d=128, causal).
@@ -436,6 +438,7 @@ def main():
 
     # ---- draft-tree verification, its own timed loop ----
     t_tree = None
+    tree_gbs = None
     if not args.skip_tree and args.only in (None, "tree"):
         wlt, part = w.tree_workload(**w.TREE_T1)
         Lt = wlt.layout
@@ -462,10 +465,11 @@ def main():
         warm_up(tcall)
         t_tree = time_calls(tcall)
         fl, by = tree_work(wlt, part)
+        tree_gbs = by / (t_tree * 1e-3) / 1e9
         out["tree"] = {"ms": round(t_tree, 4),
                        "tflops": round(fl / (t_tree * 1e-3) / 1e12, 2),
-                       "hbm_gbs": round(by / (t_tree * 1e-3) / 1e9, 1),
-                       "hbm_frac_peak": round(by / (t_tree * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "hbm_gbs": round(tree_gbs, 1),
+                       "hbm_frac_peak": round(tree_gbs / PEAK_HBM_GBS, 4),
                        "nodes": wlt.total_q, "committed_tokens": int(Lt.seq_lens.sum()) - wlt.total_q,
                        "flops": fl, "algorithmic_bytes": by,
                        "traffic": measured_traffic("tree_bf16_kernel<128> T1")}
@@ -572,6 +576,39 @@ def main():
             "frac_peak": round(gbs_cp / PEAK_HBM_GBS, 4)}
         del src, dst
         log("copy timed")
+        # and the read-only rate of the probe library (16-byte non-temporal
+        # loads): a sequential sweep and 4 KiB chunks in random order, the
+        # grain of the paged kernels' reads
+        import ctypes
+        probe = ctypes.CDLL(os.path.join(ROOT, "exact_attention_26_amd", "libfa_probe.so"))
+        probe.fa_probe_read.restype = ctypes.c_int
+        probe.fa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        nb = 2 ** 32
+        buf = torch.ones(nb, dtype=torch.uint8, device=dev)
+        order = torch.from_numpy(np.random.default_rng(12).permutation(nb // 4096)
+                                 .astype(np.int32)).to(dev)
+        sink = torch.zeros(256, dtype=torch.int32, device=dev)
+
+        def rd(order_ptr):
+            rc = probe.fa_probe_read(buf.data_ptr(), nb, order_ptr, sink.data_ptr(),
+                                     stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"fa_probe_read returned {rc}")
+        rates = {}
+        for name, ptr in (("sequential", None), ("random_4k", order.data_ptr())):
+            warm_up(lambda: rd(ptr))
+            rates[name] = nb / (time_calls(lambda: rd(ptr)) * 1e-3) / 1e9
+        out["hbm_read_ceiling"] = {
+            "kind": "read-only probe over 4 GiB (libfa_probe.so, 16-byte non-temporal loads)",
+            "sequential_gbs": round(rates["sequential"], 1),
+            "random_4k_gbs": round(rates["random_4k"], 1),
+            "frac_peak": round(rates["sequential"] / PEAK_HBM_GBS, 4),
+            "decode_over_random_4k": (round(gbs / rates["random_4k"], 4) if run_dec else None),
+            "tree_over_random_4k": (round(tree_gbs / rates["random_4k"], 4)
+                                    if tree_gbs is not None else None)}
+        del buf, order, sink
+        log("read probe timed")
 
     if args.only is not None:
         ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,

@@ -48,6 +48,26 @@ def _compile(src: str) -> str:
     return obj
 
 
+# The benchmark's HBM read-rate probe: its own library, not part of libfa.so.
+PROBE_SOURCE = "read_probe.hip"
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Build libfa_probe.so (the read-bandwidth probe bench.py reports as
+    context for the HBM-bound kernels)."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = _compile(PROBE_SOURCE)
+    out = os.path.join(HERE, "libfa_probe.so")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out + ".tmp",
+                        obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(out + ".tmp", out)
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
@@ -72,3 +92,4 @@ def build(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     build()
+    build_probe()

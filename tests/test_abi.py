@@ -41,6 +41,23 @@ def test_library_exports_every_declared_symbol():
         assert set(_declared_functions()) <= exported
 
 
+def test_read_probe_library_is_separate():
+    """The benchmark's read probe lives in its own library: libfa.so exports
+    only the attention boundary, and the probe rejects bad arguments before
+    launching anything."""
+    path = os.path.join(ROOT, "exact_attention_26_amd", "libfa_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libfa_probe.so not built")
+    probe = ctypes.CDLL(path)
+    probe.fa_probe_read.restype = ctypes.c_int
+    probe.fa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    assert not hasattr(fa.load_library(), "fa_probe_read")
+    assert probe.fa_probe_read(None, 1 << 20, None, FAKE, None) != 0
+    assert probe.fa_probe_read(FAKE, 8, None, FAKE, None) != 0
+    assert probe.fa_probe_read(FAKE, 4096 * 33, FAKE, FAKE, None) != 0   # not whole 128 KiB
+
+
 def test_status_strings_and_last_error():
     assert fa.fa_status_string(0) == "FA_OK"
     assert "INVALID" in fa.fa_status_string(1)
