@@ -10,7 +10,8 @@
 // section 3).  Under the causal mask a work group takes two blocks, a long
 // one and a short one (causal_groups), so that all work groups carry about
 // the same number of key tiles.  The block itself is fwd_block
-// (fa_fwd_block.h) over a dense K/V source.
+// (fa_fwd_block.h) over a dense K/V source, or, without the mask at d = 128,
+// fwd_block_pingpong (its two wave groups alternate matrix and vector work).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,11 +27,6 @@ __global__ __launch_bounds__(64 * dense_fwd_waves<CAUSAL>(), 8 / dense_fwd_waves
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, int N, int n_qblocks, float scale_log2) {
-    // two stages, each a K tile followed by a V tile, as separate arrays (the
-    // compiler then knows reads of one stage do not alias loads into the other)
-    __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * FwdShape<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
-
     // work group -> (batch*head, query block); XCD-aware remap (work groups are
     // dealt round-robin to 8 XCDs: give each XCD a contiguous range so the query
     // blocks of a head share one L2)
@@ -45,10 +41,6 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
     constexpr int W = dense_fwd_waves<CAUSAL>();
     constexpr int BM = 32 * W;                 // query rows per block
-    DenseKV<D, W> kv;
-    kv.K = K + base;
-    kv.V = V + base;
-    kv.len = N;
     QRows qr;
     qr.Q = Q + base;
     qr.O = O + base;
@@ -56,16 +48,34 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     qr.stride = D;
     qr.lse_stride = 1;
     qr.rows = N;
-    if (!CAUSAL) {
-        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, p * BM, 0, scale_log2);
-        return;
-    }
-    const int qb_heavy = n_qblocks - 1 - p;
-    const int n_blocks = (p < qb_heavy) ? 2 : 1;
-    for (int i = 0; i < n_blocks; ++i) {
-        if (i > 0) __syncthreads();            // the first block's last tile is read
-        fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, (i == 0 ? qb_heavy : p) * BM, 0,
-                             scale_log2);
+    constexpr int TILE = FwdShape<D>::TILE;
+    if constexpr (use_pingpong<D, CAUSAL>()) {
+        // separate arrays for the two K and two V buffers (the compiler then
+        // knows reads of one do not alias loads into another)
+        __shared__ __attribute__((aligned(1024))) uint16_t kb0[TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
+        fwd_block_pingpong<D>(kb0, kb1, vb0, vb1, qr, K + base, V + base, N, p * BM, scale_log2);
+    } else {
+        // two stages, each a K tile followed by a V tile, as separate arrays
+        __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
+        DenseKV<D, W> kv;
+        kv.K = K + base;
+        kv.V = V + base;
+        kv.len = N;
+        if constexpr (!CAUSAL) {
+            fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, p * BM, 0, scale_log2);
+        } else {
+            const int qb_heavy = n_qblocks - 1 - p;
+            const int n_blocks = (p < qb_heavy) ? 2 : 1;
+            for (int i = 0; i < n_blocks; ++i) {
+                if (i > 0) __syncthreads();    // the first block's last tile is read
+                fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, (i == 0 ? qb_heavy : p) * BM, 0,
+                                     scale_log2);
+            }
+        }
     }
 }
 

@@ -163,6 +163,12 @@ struct PagedKV {
 template <bool CAUSAL>
 __host__ __device__ constexpr int dense_fwd_waves() { return CAUSAL ? 4 : 8; }
 
+// The ping-pong block (fwd_block_pingpong) serves the non-causal dense
+// forwards at d = 128: same-box A/B 253-254 -> 246-248 us at B=8 H=16 N=2048;
+// at d = 64 it was 8-20 % slower than fwd_block.
+template <int D, bool CAUSAL>
+__host__ __device__ constexpr bool use_pingpong() { return D == 128 && !CAUSAL; }
+
 // Causal work balance: under the causal mask query block b of n sees about
 // b + 1 key tiles, so work group p of a (sequence, head) takes blocks n-1-p
 // and p (one block when they coincide); every work group then sees about the
@@ -187,6 +193,37 @@ struct QRows {
 
 // Largest draft tree of the tree mode (one 64-bit path mask per node).
 constexpr int kMaxTreeNodes = 64;
+
+// Query fragments of one lane: row qrow, elements kc*16 + 8g .. +8 for every
+// kc, as the B operand of S^T = K Q^T, sign bits flipped by qflip (a negative
+// scale); rows past qr.rows are zero.  Branch-free: such rows load the last
+// row (qr.rows >= 1 whenever a block runs) and are zeroed afterwards.  ROPE:
+// the rows are rotated on load, all table loads in flight together.
+template <int D, bool ROPE>
+__device__ __forceinline__ void load_q_operand(const QRows& qr, int qrow, int g, uint32_t qflip,
+                                               bf16x8* qop) {
+    constexpr int NKC = FwdShape<D>::NKC;
+    const int qld = min(qrow, qr.rows - 1);
+    const uint32_t keep = (qrow < qr.rows) ? 0xFFFFFFFFu : 0u;
+    u32x4 xq[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        xq[kc] = *reinterpret_cast<const u32x4*>(qr.Q + qld * qr.stride + kc * 16 + g * 8);
+    if constexpr (ROPE) {
+        // elements kc*16 + 8g .. +8 are pairs kc*8 + 4g .. +4
+        float4 cq[NKC], sq[NKC];
+        const int64_t t0 = (int64_t)(qr.pos0 + qld) * (D / 2) + g * 4;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            cq[kc] = *reinterpret_cast<const float4*>(qr.rope_cos + t0 + kc * 8);
+            sq[kc] = *reinterpret_cast<const float4*>(qr.rope_sin + t0 + kc * 8);
+        }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) xq[kc] = rotate_pairs(xq[kc], cq[kc], sq[kc]);
+    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) qop[kc] = __builtin_bit_cast(bf16x8, (xq[kc] & keep) ^ qflip);
+}
 
 // One block of 32 x KV::kWaves query rows (one wave per 32 rows) starting at
 // row q0.  Causal: row r sees the
@@ -249,32 +286,7 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
 
     // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
     bf16x8 qop[NKC];
-    {
-        // branch-free: rows past the end load the last row (qr.rows >= 1
-        // whenever a block runs) and are zeroed afterwards
-        const int qld = min(qrow, qr.rows - 1);
-        const uint32_t keep = (qrow < qr.rows) ? 0xFFFFFFFFu : 0u;
-        u32x4 xq[NKC];
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-            xq[kc] = *reinterpret_cast<const u32x4*>(qr.Q + qld * qr.stride + kc * 16 + g * 8);
-        if constexpr (ROPE) {
-            // all table loads in flight together, then the rotation: elements
-            // kc*16 + 8g .. +8 are pairs kc*8 + 4g .. +4
-            float4 cq[NKC], sq[NKC];
-            const int64_t t0 = (int64_t)(qr.pos0 + qld) * (D / 2) + g * 4;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                cq[kc] = *reinterpret_cast<const float4*>(qr.rope_cos + t0 + kc * 8);
-                sq[kc] = *reinterpret_cast<const float4*>(qr.rope_sin + t0 + kc * 8);
-            }
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) xq[kc] = rotate_pairs(xq[kc], cq[kc], sq[kc]);
-        }
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-            qop[kc] = __builtin_bit_cast(bf16x8, (xq[kc] & keep) ^ qflip);
-    }
+    load_q_operand<D, ROPE>(qr, qrow, g, qflip, qop);
 
     f32x16 oacc[ND];
 #pragma unroll
@@ -316,8 +328,8 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
     // ---- one key tile: wait for its loads, sync (all loads landed, everyone
     //      is done with the other buffer), start the next tile's loads into
     //      the other buffer, then scores, online softmax and PV on this one.
-    auto tile_step = [&](int kt, uint16_t* cur, uint16_t* nxt, auto mask_tag) __device__
-        __attribute__((always_inline)) {
+    auto tile_step = [&](int kt, uint16_t* cur, uint16_t* nxt, auto mask_tag)
+                         __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint16_t* ks = cur;
         const uint16_t* vs = cur + TILE;
@@ -454,6 +466,229 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
 
     // ---- epilogue: O = O_acc / l (bf16, round to nearest even), LSE = ln l + m;
     //      a row that saw no key (l = 0) gets O = 0, LSE = -inf
+    const float l_tot = pair_sum(l_run);
+    if (qrow < qr.rows) {
+        const bool empty = !(l_tot > 0.f);
+        const float inv = empty ? 0.f : 1.0f / l_tot;
+        uint16_t* orow = qr.O + qrow * qr.stride;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * i + 4 * g) =
+                    to_bf16x4(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv,
+                              oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+        if (qr.lse != nullptr && g == 0) {
+            const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+            qr.lse[qrow * qr.lse_stride] = empty ? kNegInf : (mc + __log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
+// ---- ping-pong block: the non-causal dense forward at d = 128 ----
+//
+// 256 query rows, 8 waves sharing every K/V tile, as fwd_block with 8 waves,
+// but the waves are two groups of four (waves 0-3: A, 4-7: B; every SIMD
+// holds one wave of each) that work half a tile apart.  Each wave alternates
+//   M(k): O += V_{k-1} P_{k-1}, then S_k = K_k Q^T        (matrix cores, LDS)
+//   V(k): online softmax of S_k into P_k                  (vector ALU)
+// and the groups run A: M(k) V(k), B: V(k-1) M(k), so in each half of an
+// iteration one wave of every SIMD issues MFMAs while the other one computes
+// exponentials: the two units overlap instead of both waves of a SIMD
+// waiting on the same phase.  Two barriers per iteration keep the groups
+// half an iteration apart; scheduling barriers keep the compiler from moving
+// MFMAs across them.  K and V tiles have two LDS buffers each: K_k and V_k
+// live in buffer k & 1, and the loads of K_{k+1} and V_k go out at the top
+// of iteration k, into buffers the previous iteration finished reading.
+// Every wave performs the same arithmetic in the same order as fwd_block, so
+// the results are bit-identical.  At d = 64 the matrix phase is half as long
+// and the barriers cost more than the overlap gains; fwd_block is used there.
+template <int D, bool ROPE = false>
+__device__ __forceinline__ void fwd_block_pingpong(uint16_t* kb0, uint16_t* kb1, uint16_t* vb0,
+                                                   uint16_t* vb1, const QRows& qr,
+                                                   const uint16_t* K, const uint16_t* V, int N,
+                                                   int q0, float scale_log2) {
+    constexpr int W = 8;
+    using Sh = FwdShape<D, W>;
+    constexpr int NKC = Sh::NKC;
+    constexpr int ND = Sh::ND;
+    constexpr int LPW = Sh::LPW;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int qrow = q0 + wave * 32 + l32;
+
+    // as in fwd_block: p = 2^(c*s - c*m), c = |scale| log2(e) (2^-100 for 0)
+    const float c = fmaxf(fabsf(scale_log2), 7.888609052210118e-31f);
+    const uint32_t qflip = (scale_log2 < 0.f) ? 0x80008000u : 0u;
+    const float tau_raw = (c > 0.f) ? kRescaleThreshold / c : __builtin_inff();
+
+    const int n_kt = (N + kFwdBN - 1) / kFwdBN;
+    const int n_full = N / kFwdBN;             // tiles without keys past the end
+    const int bytes = N * D * 2;
+
+    int gofs[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) gofs[i] = tile_load_offset<D>(wave * LPW + i, lane);
+    auto load = [&](const uint16_t* X, int kt, uint16_t* dst) __attribute__((always_inline)) {
+        load_tile_lds<LPW>(X, bytes, kt * kFwdBN * D * 2, &gofs[0], dst, wave * LPW);
+    };
+
+    load(K, 0, kb0);                           // in flight during the query loads
+
+    bf16x8 qop[NKC];
+    load_q_operand<D, ROPE>(qr, qrow, g, qflip, qop);
+
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+
+    int kofs[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) kofs[kc] = frag_offset<D>(l32, 2 * kc + g);
+    int vofs[2][ND];
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) vofs[hl][db] = trfrag_offset<D>(lane, hl, db * 32);
+
+    f32x16 sacc[2];
+    bf16x8 pop[2][2];
+
+    // M(k): O += V_{k-1} P_{k-1} (k >= 1), then S_k = K_k Q^T (k < n_kt).  P
+    // is dead before S is started, so the two never hold registers together.
+    auto m_phase = [&](int k, const uint16_t* ks, const uint16_t* vs)
+                       __attribute__((always_inline)) {
+        if (k >= 1) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const uint16_t* vb = vs + (kb * 32 + cc * 16) * D;
+#pragma unroll
+                    for (int db = 0; db < ND; ++db) {
+                        const bf16x8 a = tr_operand(vb + vofs[0][db], vb + vofs[1][db]);
+                        oacc[db] = mfma(a, pop[kb][cc], oacc[db]);
+                    }
+                }
+            // two operands (four transposed reads, DS read 0x100) ahead of the
+            // MFMAs (0x008)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 4 * ND - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        if (k < n_kt) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + kofs[kc]));
+                    sacc[kb] = mfma(a, qop[kc], sacc[kb]);
+                }
+            // four K fragment reads in flight ahead of the score MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * NKC - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+    };
+
+    // V(k): online softmax of S_k into P_k (0 <= k < n_kt), as in fwd_block;
+    // lane holds query qrow and keys 64k + 32kb + 8(r/4) + 4g + r%4
+    auto v_phase = [&](int k) __attribute__((always_inline)) {
+        if (k < 0 || k >= n_kt) return;
+        if (k >= n_full) {                     // the ragged last tile
+            const int lim = N - 1 - (k * kFwdBN + 4 * g);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = kNegInf;
+        }
+        float mt = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+        mt = pair_max(mt);
+        if (__any(mt > m_run + tau_raw)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
+                if (r & 1) ps1 += p; else ps0 += p;
+                pop[kb][r >> 3][r & 7] = (__bf16)p;
+            }
+        l_run += ps0 + ps1;
+    };
+
+    // iteration k (k = 0 .. n_kt): loads of K_{k+1} and V_k, then the two
+    // halves.  Each group runs its own loop (code of the two orders never
+    // meets at a join) and both execute the same barriers; the loop body is
+    // unrolled by two so that every LDS buffer is named statically.
+    __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): K_0 has landed
+    auto iter = [&](auto group_b, int k, uint16_t* kcur, uint16_t* knext, uint16_t* vcur,
+                    uint16_t* vprev) __attribute__((always_inline)) {
+        constexpr bool B = decltype(group_b)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();                       // last iteration's reads done, its loads landed
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < n_kt) load(K, k + 1, knext);
+        if (k < n_kt) load(V, k, vcur);
+        if constexpr (!B) m_phase(k, kcur, vprev);
+        else v_phase(k - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();          // half an iteration: the groups swap units
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!B) v_phase(k);
+        else m_phase(k, kcur, vprev);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): this wave's loads have landed
+    };
+    if (wave < 4) {
+        using GroupA = std::integral_constant<bool, false>;
+        for (int k = 0; k <= n_kt; k += 2) {
+            iter(GroupA{}, k, kb0, kb1, vb0, vb1);
+            if (k + 1 <= n_kt) iter(GroupA{}, k + 1, kb1, kb0, vb1, vb0);
+        }
+    } else {
+        using GroupB = std::integral_constant<bool, true>;
+        for (int k = 0; k <= n_kt; k += 2) {
+            iter(GroupB{}, k, kb0, kb1, vb0, vb1);
+            if (k + 1 <= n_kt) iter(GroupB{}, k + 1, kb1, kb0, vb1, vb0);
+        }
+    }
+
+    // ---- epilogue, as in fwd_block
     const float l_tot = pair_sum(l_run);
     if (qrow < qr.rows) {
         const bool empty = !(l_tot > 0.f);

@@ -52,8 +52,6 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           float* __restrict__ LSE, const float* __restrict__ rope_cos,
                           const float* __restrict__ rope_sin, int N, int n_qblocks,
                           float scale_log2) {
-    __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * FwdShape<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
     const int nwg = gridDim.x;
     int wg = blockIdx.x;
     if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
@@ -64,10 +62,7 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     constexpr int W = dense_fwd_waves<CAUSAL>();
     constexpr int BM = 32 * W;                 // query rows per block
-    DenseKV<D, W> kv;
-    kv.K = K + base;
-    kv.V = V + base;
-    kv.len = N;
+    constexpr int TILE = FwdShape<D>::TILE;
     QRows qr;
     qr.Q = Q + base;
     qr.O = O + base;
@@ -78,13 +73,28 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     qr.rope_cos = rope_cos;
     qr.rope_sin = rope_sin;
     qr.pos0 = 0;
-    // causal: the blocks n_qblocks-1-p and p (causal_groups)
-    const int qb_first = CAUSAL ? n_qblocks - 1 - p : p;
-    const int n_blocks = (CAUSAL && p < qb_first) ? 2 : 1;
-    for (int i = 0; i < n_blocks; ++i) {
-        if (i > 0) __syncthreads();            // the first block's last tile is read
-        fwd_block<D, CAUSAL, DenseKV<D, W>, false, true>(
-            smem0, smem1, qr, kv, (i == 0 ? qb_first : p) * BM, 0, scale_log2);
+    if constexpr (use_pingpong<D, CAUSAL>()) {
+        __shared__ __attribute__((aligned(1024))) uint16_t kb0[TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
+        fwd_block_pingpong<D, true>(kb0, kb1, vb0, vb1, qr, K + base, V + base, N, p * BM,
+                                    scale_log2);
+    } else {
+        __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
+        __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
+        DenseKV<D, W> kv;
+        kv.K = K + base;
+        kv.V = V + base;
+        kv.len = N;
+        // causal: the blocks n_qblocks-1-p and p (causal_groups)
+        const int qb_first = CAUSAL ? n_qblocks - 1 - p : p;
+        const int n_blocks = (CAUSAL && p < qb_first) ? 2 : 1;
+        for (int i = 0; i < n_blocks; ++i) {
+            if (i > 0) __syncthreads();        // the first block's last tile is read
+            fwd_block<D, CAUSAL, DenseKV<D, W>, false, true>(
+                smem0, smem1, qr, kv, (i == 0 ? qb_first : p) * BM, 0, scale_log2);
+        }
     }
 }
 
