@@ -68,6 +68,19 @@ def test_negative_and_zero_scale(gpu_device, d):
         assert_close(f"lse scale={scale}", lse, rl, LSE_ATOL["bf16"])
 
 
+def test_long_sequence_many_chunks(gpu_device):
+    """A 40 000-token sequence (2500 pages: 79 chunks of 32 pages in the
+    grid's second dimension) beside very short ones, sharing a prefix with its
+    neighbour; NaN-poisoned pools, every head against the oracle."""
+    lens = [40000, 3, 16, 1, 40000 - 17, 511]
+    L, q, kc, vc = _small_layout(84, lens, d=128, H=3, shared_prefix=1000)
+    say(f"decode long sequences lens={lens} max_blocks={L.max_blocks}")
+    o, lse = _decode(L, q, kc, vc, gpu_device)
+    ro, rl = paged_decode_fp64(q, kc, vc, L.block_table, L.seq_lens, scale=L.scale)
+    assert_close("o", o, ro, O_ATOL["bf16"])
+    assert_close("lse", lse, rl, LSE_ATOL["bf16"])
+
+
 def test_empty_and_clamped_and_bad_pages(gpu_device):
     lens = [0, 40, 64, 20]
     L, q, kc, vc = _small_layout(82, lens, H=2, shared_prefix=0, max_blocks=4)
