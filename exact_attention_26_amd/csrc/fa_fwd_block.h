@@ -194,6 +194,72 @@ struct QRows {
 // Largest draft tree of the tree mode (one 64-bit path mask per node).
 constexpr int kMaxTreeNodes = 64;
 
+// Online softmax of one 64-key score tile (masked keys already -inf): the
+// tile maximum (in-lane, then the partner lane of the query), a rescale of
+// (O, l) only when the row maximum grows by more than the threshold (m_run
+// is the reference maximum of O and l), then p = 2^(c*s - c*m) into the bf16
+// operand of O^T += V^T P^T and the fp32 row sum.
+template <int ND>
+__device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m_run, float& l_run,
+                                             f32x16 (&oacc)[ND], bf16x8 (&pop)[2][2], float c,
+                                             float tau_raw) {
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+    mt = pair_max(mt);
+    if (__any(mt > m_run + tau_raw)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+    }
+    const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
+            if (r & 1) ps1 += p; else ps0 += p;
+            pop[kb][r >> 3][r & 7] = (__bf16)p;
+        }
+    l_run += ps0 + ps1;                        // row sum from the fp32 probabilities
+}
+
+// S^T = K Q^T for the tile's two 32-key blocks: K fragments read from the
+// swizzled LDS tile `ks`, four reads (DS read, 0x100) kept in flight ahead of
+// the MFMAs (0x008).
+template <int D>
+__device__ __forceinline__ void score_mfmas(f32x16 (&sacc)[2], const uint16_t* ks,
+                                            const int* kofs, const bf16x8* qop) {
+    constexpr int NKC = FwdShape<D>::NKC;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + kofs[kc]));
+            sacc[kb] = mfma(a, qop[kc], sacc[kb]);
+        }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NKC - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
 // Query fragments of one lane: row qrow, elements kc*16 + 8g .. +8 for every
 // kc, as the B operand of S^T = K Q^T, sign bits flipped by qflip (a negative
 // scale); rows past qr.rows are zero.  Branch-free: such rows load the last
@@ -347,29 +413,7 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
 
         // ---- S^T = K Q^T for 2 blocks of 32 keys
         f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + kofs[kc]));
-                sacc[kb] = mfma(a, qop[kc], sacc[kb]);
-            }
-        {
-            // schedule: keep four K fragment reads (DS read, 0x100) in flight
-            // ahead of the score MFMAs (0x008)
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < 2 * NKC - 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        }
+        score_mfmas<D>(sacc, ks, kofs, qop);
         if (kt + 1 < n_kt) kv.load_v(kt + 1, nxt, wave);   // the next tile's V, staggered
 
         // ---- online softmax; lane holds query qrow and keys
@@ -403,34 +447,8 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
                     }
             }
         }
-        float mt = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-        mt = pair_max(mt);
-        if (__any(mt > m_run + tau_raw)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
-        }
-        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
         bf16x8 pop[2][2];
-        float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
-                if (r & 1) ps1 += p; else ps0 += p;
-                pop[kb][r >> 3][r & 7] = (__bf16)p;
-            }
-        l_run += ps0 + ps1;                    // row sum from the fp32 probabilities
+        softmax_tile<ND>(sacc, m_run, l_run, oacc, pop, c, tau_raw);
 
         // ---- O^T += V^T P^T.  Fragment for d rows db*32 .. +32 and keys
         //      32kb + 16cc + {4g..4g+3, 8+4g..8+4g+3}: two transpose loads.
@@ -586,28 +604,7 @@ __device__ __forceinline__ void fwd_block_pingpong(uint16_t* kb0, uint16_t* kb1,
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
-        if (k < n_kt) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-                    const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4*>(ks + kb * 32 * D + kofs[kc]));
-                    sacc[kb] = mfma(a, qop[kc], sacc[kb]);
-                }
-            // four K fragment reads in flight ahead of the score MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < 2 * NKC - 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        }
+        if (k < n_kt) score_mfmas<D>(sacc, ks, kofs, qop);
     };
 
     // V(k): online softmax of S_k into P_k (0 <= k < n_kt), as in fwd_block;
@@ -622,33 +619,7 @@ __device__ __forceinline__ void fwd_block_pingpong(uint16_t* kb0, uint16_t* kb1,
                 for (int r = 0; r < 16; ++r)
                     if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = kNegInf;
         }
-        float mt = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-        mt = pair_max(mt);
-        if (__any(mt > m_run + tau_raw)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
-        }
-        const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
-        float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
-                if (r & 1) ps1 += p; else ps0 += p;
-                pop[kb][r >> 3][r & 7] = (__bf16)p;
-            }
-        l_run += ps0 + ps1;
+        softmax_tile<ND>(sacc, m_run, l_run, oacc, pop, c, tau_raw);
     };
 
     // iteration k (k = 0 .. n_kt): loads of K_{k+1} and V_k, then the two
