@@ -136,6 +136,37 @@ def test_full_size_sampled_rows(gpu_device, name):
         del o, lse
 
 
+def test_grid_beyond_65535_work_groups(gpu_device):
+    """B=1 H=2048 N=8192 d=128: 65 536 work groups in both launch
+    configurations (2048 heads x 32 blocks of 256 rows; 2048 heads x 32 causal
+    pairs of 128-row blocks), so the 1-D grid and its XCD remap run past the
+    16-bit range.  Inputs are drawn on the device (seeded, N(0,1)); the oracle
+    gets the sampled heads' rows."""
+    import torch
+    B, H, N, d = 1, 2048, 8192, 128
+    gen = torch.Generator(device=gpu_device)
+    gen.manual_seed(2048)
+    qd, kd, vd = (torch.randn((B, H, N, d), device=gpu_device, generator=gen,
+                              dtype=torch.float32).to(torch.bfloat16) for _ in range(3))
+    rng = np.random.default_rng(2048)
+    heads = [0, 1, 1023, 2046, 2047, int(rng.integers(H))]
+    host = {h: tuple(t[0, h].float().cpu().numpy().astype(np.float64) for t in (qd, kd, vd))
+            for h in heads}
+    for causal in (False, True):
+        say(f"fwd grid B={B} H={H} N={N} d={d} causal={causal}")
+        o, lse = fa.attention(qd, kd, vd, causal=causal)
+        torch.cuda.synchronize()
+        for h in heads:
+            rows = sample_rows(N, rng)
+            q, k, v = host[h]
+            ro, rl = attention_fp64(q, k, v, causal=causal, scale=1 / math.sqrt(d), rows=rows)
+            assert_close(f"o h={h}", to_host(o[0, h, rows]), ro, O_ATOL["bf16"])
+            assert_close(f"lse h={h}", to_host(lse[0, h, rows]), rl, LSE_ATOL["bf16"])
+        del o, lse
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_sequence_sampled_rows(gpu_device, causal):
     """N = 32768 keys (512 key tiles; 128 blocks of 256 rows without the mask,
