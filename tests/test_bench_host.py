@@ -1,0 +1,91 @@
+"""bench.py's host side on the CPU: the algorithmic FLOP and byte counts the
+reported rates divide by, checked against brute-force counts on small
+workloads, and the refusal of more than one GPU (no GPU touched)."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+from exact_attention_26_amd import workloads as w
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_host", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_forward_flops_count_visible_pairs():
+    b = _bench()
+    for N in (1, 2, 7, 64, 65):
+        visible = sum(1 for i in range(N) for j in range(N) if j <= i)
+        assert b.fwd_flops(2, 3, N, 16, True) == 4.0 * 16 * 2 * 3 * visible
+        assert b.fwd_flops(2, 3, N, 16, False) == 4.0 * 16 * 2 * 3 * N * N
+        assert b.bwd_flops(1, 1, N, 8, True) == 2.5 * b.fwd_flops(1, 1, N, 8, True)
+
+
+def test_prefill_flops_count_visible_pairs():
+    b = _bench()
+    wl = w.prefill_workload(5, S=4, H=2, d=8, ctx_lens=[0, 3, 20, 1], new_lens=[5, 1, 7, 40],
+                            spare=2)
+    L = wl.layout
+    for causal in (True, False):
+        pairs = 0
+        for s in range(L.S):
+            n, tot = int(wl.new_lens[s]), int(L.seq_lens[s])
+            for i in range(n):
+                last = (tot - n + i) if causal else tot - 1
+                pairs += sum(1 for t in range(tot) if t <= last)
+        assert b.prefill_flops(wl, causal) == 4.0 * L.d * L.H * pairs
+
+
+def test_tree_work_counts_paths_and_distinct_rows():
+    b = _bench()
+    wl, parents = w.tree_workload(7, S=3, H=2, d=8, ctx_lens=[10, 0, 33], new_lens=[6, 4, 9],
+                                  shared_prefix=16, spare=2)
+    L = wl.layout
+    pairs = 0
+    for s in range(L.S):
+        lo, hi = int(wl.cu_seqlens_q[s]), int(wl.cu_seqlens_q[s + 1])
+        ctx = int(L.seq_lens[s]) - (hi - lo)
+        for i in range(hi - lo):
+            path, cur = {i}, i
+            while 0 <= int(parents[lo + cur]) < cur:
+                cur = int(parents[lo + cur])
+                path.add(cur)
+            pairs += ctx + len(path)
+    flops, nbytes = b.tree_work(wl, parents)
+    assert flops == 4.0 * L.d * L.H * pairs
+    # K/V: every distinct (physical page, slot) some node reads, once
+    rows = {(int(L.block_table[s, t // L.page_size]), t % L.page_size)
+            for s in range(L.S) for t in range(int(L.seq_lens[s]))}
+    used = {(s, p) for s in range(L.S) for p in range(-(-int(L.seq_lens[s]) // L.page_size))}
+    small = wl.total_q * L.H * (L.d * 4 + 4) + len(used) * 4 + L.S * 8 + wl.total_q * 4
+    assert nbytes == len(rows) * L.H * L.d * 4 + small
+
+
+def test_decode_bytes_count_distinct_rows_once():
+    b = _bench()
+    L = w.decode_layout(3, S=4, H=2, d=8, lens=[1, 17, 40, 40], shared_prefix=32, spare=2,
+                        len_range=(1, 40))
+    rows = {(int(L.block_table[s, t // L.page_size]), t % L.page_size)
+            for s in range(L.S) for t in range(int(L.seq_lens[s]))}
+    logical = int(L.seq_lens.sum())
+    assert len(rows) < logical                       # the pair (2, 3) shares 32 tokens
+    used = {(s, p) for s in range(L.S) for p in range(-(-int(L.seq_lens[s]) // L.page_size))}
+    small = L.S * L.H * L.d * 4 + L.S * L.H * 4 + len(used) * 4 + L.S * 4
+    alg, logi = b.decode_bytes(L)
+    assert alg == len(rows) * L.H * L.d * 4 + small
+    assert logi == logical * L.H * L.d * 4 + small
