@@ -132,6 +132,14 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_cache_dtypes(q, k_cache, v_cache):
+    """The library is told q's dtype only: the caches must share it (checked
+    before anything else, so a mismatch never reaches the kernels)."""
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError(f"k_cache and v_cache must have q's dtype ({q.dtype}); got "
+                         f"{k_cache.dtype} and {v_cache.dtype}")
+
+
 def _check_dense(name, t, device):
     if not t.is_cuda or t.device != device:
         raise ValueError(f"{name} must be on {device}")
@@ -192,6 +200,7 @@ def fa_paged_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale: f
     ``seq_lens`` int32 [S]; ``lse`` float32 [S][H] or None; ``workspace`` a
     uint8 device tensor of at least ``fa_paged_decode_workspace_size`` bytes."""
     torch = _torch()
+    _check_cache_dtypes(q, k_cache, v_cache)
     S, H, d = q.shape
     nb, Hk, P, dk = k_cache.shape
     dev = q.device
@@ -227,6 +236,7 @@ def fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o
     ``seq_lens`` int32 [S]; ``cu_seqlens_q`` int32 [S+1]; ``lse`` float32
     [total_q][H] or None."""
     torch = _torch()
+    _check_cache_dtypes(q, k_cache, v_cache)
     total_q, H, d = q.shape
     nb, Hk, P, dk = k_cache.shape
     dev = q.device
@@ -261,6 +271,7 @@ def fa_tree_decode(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, tre
     """Call ``fa_tree_decode``: as ``fa_paged_prefill`` plus ``tree_parents``
     (int32 [total_q], each node's parent among its sequence's nodes or -1)."""
     torch = _torch()
+    _check_cache_dtypes(q, k_cache, v_cache)
     _check_dense("tree_parents", tree_parents, q.device)
     if tree_parents.dtype != torch.int32 or tuple(tree_parents.shape) != (q.shape[0],):
         raise ValueError("tree_parents must be int32 [total_q]")

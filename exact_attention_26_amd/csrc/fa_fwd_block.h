@@ -293,8 +293,9 @@ __device__ __forceinline__ void load_q_operand(const QRows& qr, int qrow, int g,
 
 // One block of 32 x KV::kWaves query rows (one wave per 32 rows) starting at
 // row q0.  Causal: row r sees the
-// keys 0 .. shift + r (shift = 0 for square attention; for new tokens at the
-// end of a sequence of kv.len tokens, shift = kv.len - rows).  TREE: the rows
+// keys 0 .. shift + r (shift = 0 for square attention; for the last n tokens
+// of a sequence of kv.len tokens, shift = kv.len - n, however many of those
+// n rows are computed).  TREE: the rows
 // are the nodes of a draft tree whose K/V are the last `rows` keys; row r
 // sees the keys before `shift` (the committed tokens) and the tree keys of
 // the nodes on its path from the root, found by walking `parents` (node r's

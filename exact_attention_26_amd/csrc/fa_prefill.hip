@@ -49,9 +49,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     int qb = k - j * n_qblocks;
     if (CAUSAL) qb = n_qblocks - 1 - qb;
 
-    // this sequence's new rows, kept inside [0, total_q)
+    // this sequence's new tokens (their positions follow from n_new), of
+    // which the rows inside [0, total_q) are computed
     const int qbeg = cu_q[s];
-    int rows = cu_q[s + 1] - qbeg;
+    const int n_new = max(0, cu_q[s + 1] - qbeg);
+    int rows = n_new;
     if (qbeg < 0 || qbeg >= total_q) rows = 0;
     rows = max(0, min(rows, total_q - qbeg));
     const int q0 = qb * kFwdBM;
@@ -73,8 +75,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     qr.stride = (int64_t)H * D;
     qr.lse_stride = H;
     qr.rows = rows;
-    // the new tokens are the last `rows` of the L cached ones
-    fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, q0, L - rows, scale_log2);
+    // the new tokens are the last n_new of the L cached ones; row r stands at
+    // position L - n_new + r whether or not later rows are computed
+    fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, q0, L - n_new, scale_log2);
 }
 
 // Batches of up to this many sequences are verified longest first.
@@ -138,8 +141,11 @@ void tree_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
                                            len_sh, &pick)
                       : t;
 
+    // the tree's nodes (their positions follow from n_nodes), of which the
+    // first kMaxTreeNodes inside [0, total_q) are computed
     const int qbeg = cu_q[s];
-    int rows = cu_q[s + 1] - qbeg;
+    const int n_nodes = max(0, cu_q[s + 1] - qbeg);
+    int rows = n_nodes;
     if (qbeg < 0 || qbeg >= total_q) rows = 0;
     rows = max(0, min(min(rows, total_q - qbeg), kMaxTreeNodes));
     if (rows == 0) return;
@@ -161,8 +167,9 @@ void tree_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     qr.stride = (int64_t)H * D;
     qr.lse_stride = H;
     qr.rows = rows;
-    // the tree's K/V are the last `rows` of the L cached tokens
-    fwd_block<D, false, PagedKV<D, true>, true>(smem0, smem1, qr, kv, 0, L - rows, scale_log2,
+    // the tree's K/V are the last n_nodes of the L cached tokens (keys of
+    // nodes past kMaxTreeNodes are hidden: no computed node has them on its path)
+    fwd_block<D, false, PagedKV<D, true>, true>(smem0, smem1, qr, kv, 0, L - n_nodes, scale_log2,
                                                 parents + qbeg);
 }
 

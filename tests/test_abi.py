@@ -227,3 +227,28 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setenv("FA_LIBRARY", str(tmp_path / "missing.so"))
     with pytest.raises(fa.FaError):
         b.load_library()
+
+
+@pytest.mark.parametrize("entry", ["decode", "prefill", "tree"])
+@pytest.mark.parametrize("bad", ["k", "v"])
+def test_binding_rejects_cache_dtype_mismatch(entry, bad):
+    """The library is told q's dtype only, so a float32 cache passed with a
+    bf16 q would be read as bf16: the binding refuses it before any call."""
+    import torch
+    q = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
+    good = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16)
+    wrong = torch.zeros((4, 2, 16, 64), dtype=torch.float32)
+    kc, vc = (wrong, good) if bad == "k" else (good, wrong)
+    table = torch.zeros((3, 4), dtype=torch.int32)
+    lens = torch.ones(3, dtype=torch.int32)
+    cu = torch.arange(4, dtype=torch.int32)
+    o = torch.empty_like(q)
+    with pytest.raises(ValueError, match="dtype"):
+        if entry == "decode":
+            fa.fa_paged_decode(q, kc, vc, table, lens, o, None, 0.125,
+                               torch.empty(64, dtype=torch.uint8))
+        elif entry == "prefill":
+            fa.fa_paged_prefill(q, kc, vc, table, lens, cu, o, None, 1, True, 0.125)
+        else:
+            fa.fa_tree_decode(q, kc, vc, table, lens, cu, torch.full((3,), -1, dtype=torch.int32),
+                              o, None, 1, 0.125)

@@ -166,3 +166,34 @@ def test_prefill_deterministic(gpu_device):
     a = _run(wl, q, kc, vc, True, gpu_device)
     b = _run(wl, q, kc, vc, True, gpu_device)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_rows_past_total_q_keep_positions(gpu_device, causal):
+    """Device data whose last sequence runs past total_q (cu_seqlens_q[S] >
+    total_q): the rows inside are computed at their true positions (the new
+    tokens are still the last n_s cached ones) and nothing past total_q is
+    touched."""
+    import torch
+    new = [30, 150]
+    wl = w.prefill_workload(621, S=2, H=2, d=128, ctx_lens=[20, 60], new_lens=new, spare=4)
+    q = w.prefill_q(wl)
+    kc, vc = _pools(wl)
+    L = wl.layout
+    total_q = 30 + 100                         # 50 of sequence 1's rows lie past the end
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(gpu_device)  # noqa: E731
+    qd = to_dev(q, "bf16", gpu_device)
+    o = torch.full((wl.total_q, L.H, L.d), 7.0, dtype=torch.bfloat16, device=gpu_device)
+    lse = torch.full((wl.total_q, L.H), 7.0, dtype=torch.float32, device=gpu_device)
+    say(f"prefill rows past total_q causal={causal}")
+    fa.fa_paged_prefill(qd[:total_q], to_dev(kc, "bf16", gpu_device),
+                        to_dev(vc, "bf16", gpu_device), t(L.block_table), t(L.seq_lens),
+                        t(wl.cu_seqlens_q), o[:total_q], lse[:total_q], wl.max_q_len, causal,
+                        L.scale)
+    torch.cuda.synchronize()
+    o, lse = to_host(o), to_host(lse)
+    want = paged_prefill_fp64(q, kc, vc, L.block_table, L.seq_lens, wl.cu_seqlens_q,
+                              causal=causal, scale=L.scale)
+    _check("rows inside total_q", (o[:total_q], lse[:total_q]),
+           (want[0][:total_q], want[1][:total_q]))
+    assert np.all(o[total_q:] == 7.0) and np.all(lse[total_q:] == 7.0)

@@ -128,3 +128,30 @@ def test_tree_deterministic_and_rejects_big_trees(gpu_device):
     with pytest.raises(fa.FaError) as e:
         _run(wl, parents, q, kc, vc, gpu_device, max_q_len=65)
     assert e.value.status == 2
+
+
+def test_tree_more_nodes_than_the_limit_keeps_positions(gpu_device):
+    """Device data with 70 nodes in a sequence (max_q_len says 64): nodes
+    0..63 are computed at their true positions (the tree's K/V are still the
+    last 70 cached tokens) and nodes 64..69 are not written."""
+    import torch
+    wl, parents = w.tree_workload(731, S=2, H=2, d=128, ctx_lens=[100, 40], new_lens=[70, 10],
+                                  spare=4)
+    q = w.prefill_q(wl)
+    kc = w.decode_pool(wl.layout, "k", poison=True)
+    vc = w.decode_pool(wl.layout, "v", poison=True)
+    L = wl.layout
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(gpu_device)  # noqa: E731
+    o = torch.full((wl.total_q, L.H, L.d), 7.0, dtype=torch.bfloat16, device=gpu_device)
+    lse = torch.full((wl.total_q, L.H), 7.0, dtype=torch.float32, device=gpu_device)
+    say("tree 70 nodes, max_q_len 64")
+    fa.fa_tree_decode(to_dev(q, "bf16", gpu_device), to_dev(kc, "bf16", gpu_device),
+                      to_dev(vc, "bf16", gpu_device), t(L.block_table), t(L.seq_lens),
+                      t(wl.cu_seqlens_q), t(parents.astype(np.int32)), o, lse, 64, L.scale)
+    torch.cuda.synchronize()
+    o, lse = to_host(o), to_host(lse)
+    want = tree_decode_fp64(q, kc, vc, L.block_table, L.seq_lens, wl.cu_seqlens_q, parents,
+                            scale=L.scale)
+    done = np.r_[0:64, 70:80]
+    _check("first 64 nodes", (o[done], lse[done]), (want[0][done], want[1][done]))
+    assert np.all(o[64:70] == 7.0) and np.all(lse[64:70] == 7.0), "nodes past 64 were written"
