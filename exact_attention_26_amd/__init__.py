@@ -8,8 +8,9 @@ stream) into the C calls and raises if a call reports an error.  Nothing here
 computes attention; if the shared library is missing the calls raise.
 """
 from ._binding import (  # noqa: F401
-    FA_BF16, FA_F32, FaError, attention, attention_backward, fa_bwd, fa_bwd_workspace_size,
-    fa_fwd, fa_paged_decode, fa_paged_decode_workspace_size, fa_paged_prefill, fa_status_string,
+    FA_BF16, FA_ERR_TOO_LARGE, FA_F32, FA_NOALLOC_SCRATCH_BYTES, FaError, attention,
+    attention_backward, fa_bwd, fa_bwd_workspace_size, fa_fwd, fa_paged_decode,
+    fa_paged_decode_noalloc, fa_paged_decode_workspace_size, fa_paged_prefill, fa_status_string,
     fa_last_hip_error, fa_tree_decode, library_path, load_library, paged_decode, paged_prefill,
     tree_decode, fa_rope, fa_fwd_rope, fa_fwd_rope_workspace_size, rope, attention_rope,
 )

@@ -11,7 +11,8 @@ import ctypes
 import math
 import os
 
-FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20     # scratch fa_paged_decode_noalloc holds per GPU
 FA_BF16, FA_F32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,9 @@ def load_library():
                                     c.c_void_p, c.c_void_p,
                                     c.c_int, c.c_int, c.c_int, c.c_int, c.c_int, c.c_int64,
                                     c.c_float, c.c_int, c.c_void_p, c.c_size_t, c.c_void_p]
+    lib.fa_paged_decode_noalloc.restype = c.c_int
+    lib.fa_paged_decode_noalloc.argtypes = [c.c_void_p] * 7 + [c.c_int] * 5 + [c.c_int64,
+                                                                c.c_float, c.c_int, c.c_void_p]
     lib.fa_paged_prefill.restype = c.c_int
     lib.fa_paged_prefill.argtypes = [c.c_void_p] * 8 + [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int,
                                                         c.c_int64, c.c_int, c.c_int, c.c_int,
@@ -227,6 +231,39 @@ def fa_paged_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale: f
         _dtype_code(q), _ptr(workspace), ws_bytes, _stream(dev))
     if st != FA_OK:
         raise FaError(st, "fa_paged_decode")
+
+
+def fa_paged_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse,
+                            scale: float) -> None:
+    """Call ``fa_paged_decode_noalloc``: ``fa_paged_decode`` without a
+    workspace (the library's per-GPU scratch array holds the partials; calls
+    that overlap on one GPU race).  Allocates nothing."""
+    torch = _torch()
+    _check_cache_dtypes(q, k_cache, v_cache)
+    S, H, d = q.shape
+    nb, Hk, P, dk = k_cache.shape
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens), ("o", o)):
+        _check_dense(name, t, dev)
+    if (Hk, dk) != (H, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [num_blocks][H][page_size][d]")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != S or tuple(seq_lens.shape) != (S,):
+        raise ValueError("block_table must be [S][max_blocks], seq_lens [S]")
+    if tuple(o.shape) != (S, H, d) or o.dtype != q.dtype:
+        raise ValueError("o must match q")
+    if lse is not None:
+        _check_dense("lse", lse, dev)
+        if tuple(lse.shape) != (S, H) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [S][H]")
+    st = load_library().fa_paged_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(o), _ptr(lse), S, H, d, P, block_table.shape[1], nb, float(scale),
+        _dtype_code(q), _stream(dev))
+    if st != FA_OK:
+        raise FaError(st, "fa_paged_decode_noalloc")
 
 
 def fa_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse,

@@ -64,6 +64,22 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
                                              static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                  float* lse, int num_seqs, int H, int d, int page_size,
+                                  int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                  int dtype, void* stream) {
+    const fa_status st = fa_host::check_decode_noalloc(q, k_cache, v_cache, block_table,
+                                                       seq_lens, o, num_seqs, H, d, page_size,
+                                                       max_blocks_per_seq, num_blocks, scale,
+                                                       dtype);
+    if (st != FA_OK) return st;
+    return hip_status(fa_launch_paged_decode_scratch(q, k_cache, v_cache, block_table, seq_lens,
+                                                     o, lse, num_seqs, H, d, max_blocks_per_seq,
+                                                     num_blocks, scale,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* seq_lens,
                            const int32_t* cu_seqlens_q, void* o, float* lse, int num_seqs, int H,

@@ -32,6 +32,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
+#include "fa.h"
 #include "fa_kernels.h"
 
 namespace {
@@ -306,6 +310,60 @@ hipError_t launch(const void* q, const void* k_cache, const void* v_cache, const
 }
 
 }  // namespace
+
+// Partials of the allocation-free entry point: one array per GPU, held until
+// the process ends.  In host code `scratch` is a stand-in, not a device
+// address; the kernels get the address hipGetSymbolAddress returns for the
+// launching device (scratch_on).
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the scratch array on the device of `stream`, looked up
+// once per device with that device current.
+hipError_t scratch_on(hipStream_t stream, float** out) {
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int cur = 0;
+            e = hipGetDevice(&cur);
+            if (e != hipSuccess) return e;
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            const hipError_t back = (cur != dev) ? hipSetDevice(cur) : hipSuccess;
+            if (e != hipSuccess) return e;
+            if (back != hipSuccess) return back;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = static_cast<float*>(p);
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t fa_launch_paged_decode_scratch(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          void* o, float* lse, int S, int H, int d,
+                                          int max_blocks, int64_t num_blocks, float scale,
+                                          hipStream_t stream) {
+    float* ws = nullptr;
+    const hipError_t e = scratch_on(stream, &ws);
+    if (e != hipSuccess) return e;
+    return fa_launch_paged_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, S, H, d,
+                                  max_blocks, num_blocks, scale, ws, stream);
+}
 
 hipError_t fa_launch_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens,

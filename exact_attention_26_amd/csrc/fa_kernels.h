@@ -49,3 +49,10 @@ hipError_t fa_launch_paged_decode(const void* q, const void* k_cache, const void
                                   void* o, float* lse, int S, int H, int d,
                                   int max_blocks, int64_t num_blocks, float scale,
                                   float* workspace, hipStream_t stream);
+// The same decode with the partials in the library's static scratch array
+// (fa_decode.hip); the caller has checked that they fit.
+hipError_t fa_launch_paged_decode_scratch(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          void* o, float* lse, int S, int H, int d,
+                                          int max_blocks, int64_t num_blocks, float scale,
+                                          hipStream_t stream);

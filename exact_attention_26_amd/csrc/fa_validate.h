@@ -112,6 +112,21 @@ inline fa_status check_decode(const void* q, const void* kc, const void* vc, con
     return FA_OK;
 }
 
+// The allocation-free decode: the same checks, then the workspace must fit
+// the library's scratch array (FA_NOALLOC_SCRATCH_BYTES).
+inline fa_status check_decode_noalloc(const void* q, const void* kc, const void* vc,
+                                      const void* table, const void* lens, const void* o, int S,
+                                      int H, int d, int page_size, int max_blocks,
+                                      int64_t num_blocks, float scale, int dtype) {
+    static const char placeholder = 0;   // stands for the scratch array in the shared checks
+    const fa_status st = check_decode(q, kc, vc, table, lens, o, S, H, d, page_size, max_blocks,
+                                      num_blocks, scale, dtype, &placeholder, SIZE_MAX);
+    if (st != FA_OK) return st;
+    if (decode_workspace_bytes(S, H, d, page_size, max_blocks) > FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_TOO_LARGE;
+    return FA_OK;
+}
+
 inline fa_status check_prefill(const void* q, const void* kc, const void* vc, const void* table,
                                const void* lens, const void* cu, const void* o, int S, int H,
                                int d, int page_size, int max_blocks, int64_t num_blocks,
@@ -197,6 +212,9 @@ inline const char* status_string(int s) {
         case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid argument";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this configuration";
         case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call failed";
+        case FA_ERR_TOO_LARGE:
+            return "FA_ERR_TOO_LARGE: the call needs more than the 32 MiB of scratch memory "
+                   "the allocation-free entry point holds";
         default: return "unknown fa_status";
     }
 }

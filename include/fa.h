@@ -66,8 +66,13 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID = 1,      /* malformed arguments (null pointer, size < 1, non-finite scale, ...) */
     FA_ERR_UNSUPPORTED = 2,  /* well-formed, but no kernel for this head size / dtype / page size */
-    FA_ERR_HIP = 3           /* a HIP runtime call failed; see fa_last_hip_error() */
+    FA_ERR_HIP = 3,          /* a HIP runtime call failed; see fa_last_hip_error() */
+    FA_ERR_TOO_LARGE = 4     /* fa_paged_decode_noalloc only: the call needs more scratch
+                                memory than the library holds (FA_NOALLOC_SCRATCH_BYTES) */
 } fa_status;
+
+/* Device scratch memory that fa_paged_decode_noalloc holds on every GPU it runs on. */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum {
     FA_BF16 = 0,             /* bfloat16 inputs and outputs, float32 accumulation */
@@ -213,6 +218,41 @@ fa_status fa_paged_decode(const void* q, const void* k_cache, const void* v_cach
                           int max_blocks_per_seq, int64_t num_blocks, float scale,
                           int dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * fa_paged_decode_noalloc - fa_paged_decode for callers that cannot allocate.
+ *
+ * For callers that cannot call hipMalloc around an attention call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results as fa_paged_decode, minus the workspace:
+ * the per-split partial results live in a scratch array of
+ * FA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library keeps in device memory,
+ * one copy per GPU, held from the first call on that GPU until the process
+ * ends.  The call allocates nothing (no hipMalloc / hipFree); its first call
+ * on a GPU looks up that GPU's copy once (hipGetSymbolAddress).
+ *
+ *   requirement  fa_paged_decode_workspace_size(num_seqs, H, d, page_size,
+ *                max_blocks_per_seq) <= FA_NOALLOC_SCRATCH_BYTES, i.e.
+ *                num_seqs * H * ceil(max_blocks_per_seq / 32) * (d + 2) * 4
+ *                bytes: e.g. 64 sequences x 32 heads of d = 128 with up to
+ *                16384-token tables need 17 MB.  Larger requests return
+ *                FA_ERR_TOO_LARGE and launch nothing.
+ *   sharing      every call on one GPU uses that GPU's single array, which
+ *                keeps the last call's contents (each call writes every entry
+ *                it reads, so nothing needs clearing).  Calls that overlap in
+ *                time on one GPU (several streams or threads) race on it and
+ *                give wrong results: issue them on one stream, or serialise.
+ *   stream       the array of the stream's device is used.
+ *
+ * Returns FA_OK, FA_ERR_INVALID / FA_ERR_UNSUPPORTED as fa_paged_decode (less
+ * the workspace checks), FA_ERR_TOO_LARGE, or FA_ERR_HIP.
+ */
+fa_status fa_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  void* o, float* lse,
+                                  int num_seqs, int H, int d, int page_size,
+                                  int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                  int dtype, void* stream);
 
 /*
  * fa_paged_prefill - new query tokens of several sequences against a paged KV cache.

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
         "fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_paged_decode",
         "fa_paged_decode_workspace_size", "fa_paged_prefill", "fa_status_string",
         "fa_last_hip_error", "fa_tree_decode", "fa_rope", "fa_fwd_rope_workspace_size",
-        "fa_fwd_rope"])
+        "fa_fwd_rope", "fa_paged_decode_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -252,3 +252,39 @@ def test_binding_rejects_cache_dtype_mismatch(entry, bad):
         else:
             fa.fa_tree_decode(q, kc, vc, table, lens, cu, torch.full((3,), -1, dtype=torch.int32),
                               o, None, 1, 0.125)
+
+
+def _decode_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, table=FAKE, lens=FAKE, o=FAKE, lse=None, S=2, H=2, d=128,
+             page_size=16, max_blocks=4, num_blocks=8, scale=0.1, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.load_library().fa_paged_decode_noalloc(
+        a["q"], a["kc"], a["vc"], a["table"], a["lens"], a["o"], a["lse"], a["S"], a["H"],
+        a["d"], a["page_size"], a["max_blocks"], a["num_blocks"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(table=None), 1), (dict(S=0), 1), (dict(num_blocks=0), 1),
+    (dict(scale=float("nan")), 1), (dict(d=96), 2), (dict(page_size=8), 2),
+    (dict(dtype=fa.FA_F32), 2),
+    # d = 128: 520 bytes per (sequence, head, split of 32 pages); 64 x 32 heads with
+    # 32 splits need 34 MB, and one (sequence, head) with 64 528 splits 1 byte too many
+    (dict(S=64, H=32, max_blocks=32 * 32), 4),
+    (dict(S=1, H=1, max_blocks=32 * (((32 << 20) // 520) + 1)), 4),
+])
+def test_decode_noalloc_rejects_before_launch(kw, status):
+    """The allocation-free decode checks what fa_paged_decode checks (less the
+    workspace) and refuses, with FA_ERR_TOO_LARGE, any call whose partials do
+    not fit its 32 MiB scratch array -- all before touching the GPU."""
+    assert _decode_noalloc(**kw) == status
+
+
+def test_decode_noalloc_limit_matches_the_workspace_size():
+    """The largest call that fits needs exactly what fa_paged_decode's workspace
+    for the same sizes would hold, up to FA_NOALLOC_SCRATCH_BYTES."""
+    splits = (32 << 20) // 520                    # d = 128: 520 bytes per split
+    assert fa.fa_paged_decode_workspace_size(1, 1, 128, 16, 32 * splits) <= \
+        fa.FA_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_paged_decode_workspace_size(1, 1, 128, 16, 32 * (splits + 1)) > \
+        fa.FA_NOALLOC_SCRATCH_BYTES
+    assert "TOO_LARGE" in fa.fa_status_string(4)
