@@ -25,9 +25,20 @@ clock its published peak assumes), "hbm_ceiling" what a plain 2 GiB device
 copy reaches against the published HBM bandwidth, and "hbm_read_ceiling" what a
 read-only probe (libfa_probe.so) reaches sequentially and over 4 KiB chunks in
 random order, the grain of the paged kernels' reads.  "sweep" times the forward
-on the other configurations: the sequence sweep at 16k tokens (N = 512 ..
-16384, H=32, d=64, both masks) and the long-context one (B=1 H=16 N=16384
-d=128, causal).
+on the other configurations, on their seeded inputs: the sequence sweep at 16k
+tokens (N = 512 .. 16384, H=32, d=64, both masks) and the long-context one
+(B=1 H=16 N=16384 d=128, causal).  The decode is also timed with 512 MiB
+written between calls ("decode.flushed"), so that no call finds the previous
+call's pages in the last-level cache.
+
+"cpu_baseline" is the fp64 oracle timed on this host before the GPU is used:
+every (b, h) head of the forward bench in both masks and every (sequence, head)
+pair of the decode, over a process pool of one worker per core of the
+process's affinity (BLAS pinned to one thread each); it reports the core
+count, the BLAS library and both rates.  "parity" holds the max-abs errors of
+O and LSE against that oracle for every configuration: the fp32 smoke one in
+full, the forward bench at sampled rows of every head, the sweep and the
+long-context one at sampled rows of two heads, the decode in full.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--min-warmup-s 1.0]
                     [--no-cpu-baseline] [--skip-bwd] [--skip-prefill] [--skip-tree] [--skip-rope]
@@ -137,36 +148,169 @@ def measured_traffic(kernel_key: str):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(budget_s: float = 20.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the forward
-    workload (B=8 H=16 N=2048 d=128): whole (b, h) heads, non-causal then
-    causal, one after another until the time budget is used or every head of
-    both modes is done.  Rate = algorithmic FLOPs of the heads done / time."""
-    from exact_attention_26_amd import workloads as w
-    from oracle import attention_fp64
+# ---------------------------------------------------------------------------
+# the CPU baseline leg: the fp64 oracle timed on this host, and the GPU results
+# checked against it.  Nothing outside these functions touches the oracle.
+# ---------------------------------------------------------------------------
+_ORC = {}                       # host inputs the forked oracle workers read
+
+
+def _blas_info():
+    """BLAS library numpy uses, and its thread count in this process."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
+        infos = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if infos:
+            p = infos[0]
+            return (f"{p.get('internal_api')} {p.get('version')} ({p.get('architecture')}, "
+                    f"{p.get('threading_layer')})", max(x.get("num_threads", 1) for x in infos))
     except Exception:
-        threads = None
-    cfg = w.FWD_CONFIGS["fwd_b8_h16_n2048_d128"]
-    q, k, v = w.fwd_config_inputs(cfg)
-    done = {False: 0, True: 0}
+        pass
+    return f"numpy {np.__version__}, BLAS not identified", None
+
+
+def _oracle_worker_init():
+    """One BLAS thread per worker: the pool supplies the parallelism."""
+    global _ORC_LIMIT
+    from threadpoolctl import threadpool_limits
+    _ORC_LIMIT = threadpool_limits(1)
+
+
+def _oracle_fwd_head(task):
+    """One (b, h) head of the forward bench workload: the full oracle, timed;
+    returns the rows in _ORC['c1_rows'] for the parity check."""
+    from oracle import attention_fp64
+    causal, b, h = task
+    q, k, v, scale = _ORC["c1"]
     t0 = time.perf_counter()
-    for causal in (False, True):
-        for b in range(cfg.B):
-            for h in range(cfg.H):
-                if time.perf_counter() - t0 > budget_s:
-                    break
-                attention_fp64(q[b, h], k[b, h], v[b, h], causal=causal, scale=cfg.scale)
-                done[causal] += 1
+    o, lse = attention_fp64(q[b, h], k[b, h], v[b, h], causal=causal, scale=scale)
     dt = time.perf_counter() - t0
-    flops = fwd_flops(1, done[False], cfg.N, cfg.d, False) + fwd_flops(1, done[True], cfg.N, cfg.d, True)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle",
-            "sample": f"{done[False]} non-causal + {done[True]} causal of 2x{cfg.B * cfg.H} (b,h) "
-                      f"heads of the forward B=8 H=16 N=2048 d=128, fp64 numpy, {dt:.1f} s"}
+    rows = _ORC["c1_rows"]
+    return dt, o[rows], lse[rows]
+
+
+def _oracle_decode(task):
+    """Some (sequence, head) pairs of the decode workload, timed."""
+    from oracle import paged_decode_fp64
+    q, kc, vc, table, lens, scale = _ORC["c4"]
+    t0 = time.perf_counter()
+    o, lse = paged_decode_fp64(q, kc, vc, table, lens, scale=scale, pairs=task)
+    return time.perf_counter() - t0, o, lse
+
+
+def cpu_baseline_run(cfg, c1, c4_layout, c4_pools, c4_q):
+    """Time the oracle, as it stands, on the host cores: every (b, h) head of
+    the forward bench workload in both masks, and every (sequence, head) pair of
+    the paged decode, mapped over a process pool (one worker per core of this
+    process's affinity, BLAS pinned to one thread each).  Must run before the
+    GPU is touched (the pool is forked).  Returns the report and the oracle's
+    results for the parity check."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    blas, blas_threads = _blas_info()
+    q, k, v = c1
+    _ORC["c1"] = (q, k, v, cfg.scale)
+    _ORC["c1_rows"] = _parity_rows(cfg.N)
+    L = c4_layout
+    _ORC["c4"] = (c4_q, c4_pools[0], c4_pools[1], L.block_table, L.seq_lens, L.scale)
+    tasks = [(causal, b, h) for causal in (False, True) for b in range(cfg.B) for h in range(cfg.H)]
+    pairs = [(s, h) for s in range(L.S) for h in range(L.H)]
+    chunks = [pairs[i:i + 16] for i in range(0, len(pairs), 16)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_oracle_worker_init) as pool:
+        t0 = time.perf_counter()
+        fwd = pool.map(_oracle_fwd_head, tasks, chunksize=1)
+        t_fwd = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        dec = pool.map(_oracle_decode, chunks, chunksize=1)
+        t_dec = time.perf_counter() - t0
+    n = len(tasks) // 2
+    flops = fwd_flops(1, n, cfg.N, cfg.d, False) + fwd_flops(1, n, cfg.N, cfg.d, True)
+    dec_bytes, _ = decode_bytes(L)
+    report = {
+        "value": flops / t_fwd / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"all {n} (b,h) heads of the forward B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} "
+                   f"in both masks ({2 * n} oracle calls), fp64 numpy oracle, {cores} worker "
+                   f"processes, {t_fwd:.1f} s wall"),
+        "workers": cores, "blas": blas, "blas_threads_in_parent": blas_threads,
+        "blas_threads_per_worker": 1,
+        "decode": {"value": dec_bytes / t_dec / 1e9, "unit": "GB/s",
+                   "sample": (f"all {len(pairs)} (sequence, head) pairs of the paged decode "
+                              f"S={L.S} H={L.H} d={L.d}, {t_dec:.1f} s wall"),
+                   "seconds": round(t_dec, 3)},
+        "seconds": round(t_fwd, 3)}
+    oracle = {
+        "c1": {(causal, b, h): (o, l) for (causal, b, h), (_, o, l) in zip(tasks, fwd)},
+        "c4": (np.concatenate([o for _, o, _ in dec]).reshape(L.S, L.H, L.d),
+               np.concatenate([l for _, _, l in dec]).reshape(L.S, L.H))}
+    return report, oracle
+
+
+def _parity_rows(N):
+    """Query rows sampled for the parity check: wave and block edges, the
+    middle, the end, and a seeded random dozen."""
+    rng = np.random.default_rng(77)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, N // 2, N - 2, N - 1]
+    rows = np.concatenate([np.array(fixed), rng.choice(N, size=min(12, N), replace=False)])
+    return np.unique(np.clip(rows, 0, N - 1))
+
+
+def _max_abs(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    fin = np.isfinite(want)
+    if not np.array_equal(np.isfinite(got), fin) or not np.array_equal(got[~fin], want[~fin]):
+        return float("inf")
+    return float(np.max(np.abs(got[fin] - want[fin]))) if fin.any() else 0.0
+
+
+def cpu_baseline_parity(samples, oracle, c4_layout):
+    """Max-abs error of the GPU results on O and LSE against the oracle, per
+    configuration: the smoke one in full, the forward bench at the sampled rows
+    of every head (both masks), the sweep and the long-context one at the
+    sampled rows of two heads per mode, the decode in full."""
+    from oracle import attention_fp64
+    out = {}
+    smoke = samples.get("smoke")
+    if smoke is not None:
+        (q, k, v, scale), (o, lse) = smoke
+        ro, rl = attention_fp64(q, k, v, causal=False, scale=scale)
+        out["smoke B=1 H=2 N=256 d=64 fp32"] = {"o_max_abs": _max_abs(o, ro),
+                                                "lse_max_abs": _max_abs(lse, rl), "rows": "all"}
+    c1 = samples.get("c1")
+    if c1 is not None and oracle is not None:
+        for causal in (False, True):
+            eo = el = 0.0
+            for (cz, b, h), (ro, rl) in oracle["c1"].items():
+                if cz != causal:
+                    continue
+                go, gl = c1[causal]
+                eo = max(eo, _max_abs(go[b, h], ro))
+                el = max(el, _max_abs(gl[b, h], rl))
+            out[f"fwd B=8 H=16 N=2048 d=128 {'causal' if causal else 'non-causal'}"] = {
+                "o_max_abs": eo, "lse_max_abs": el,
+                "rows": f"{len(_parity_rows(2048))} sampled rows of all 128 heads"}
+    for name, (cfgc, heads, rows, modes) in samples.get("sweep", {}).items():
+        for causal, (q, k, v, go, gl) in modes.items():
+            eo = el = 0.0
+            for i, (b, h) in enumerate(heads):
+                ro, rl = attention_fp64(q[i], k[i], v[i], causal=causal, scale=cfgc.scale,
+                                        rows=rows)
+                eo = max(eo, _max_abs(go[i], ro))
+                el = max(el, _max_abs(gl[i], rl))
+            out[f"{name} {'causal' if causal else 'non-causal'}"] = {
+                "o_max_abs": eo, "lse_max_abs": el,
+                "rows": f"{len(rows)} sampled rows of heads {heads}"}
+    dec = samples.get("c4")
+    if dec is not None and oracle is not None:
+        ro, rl = oracle["c4"]
+        out["paged decode S=64 H=32 d=128"] = {"o_max_abs": _max_abs(dec[0], ro),
+                                               "lse_max_abs": _max_abs(dec[1], rl),
+                                               "rows": "all (sequence, head) pairs"}
+    for v in out.values():
+        v["o_max_abs"] = float(f"{v['o_max_abs']:.3e}")
+        v["lse_max_abs"] = float(f"{v['lse_max_abs']:.3e}")
+    return out
 
 
 def main():
@@ -206,6 +350,29 @@ def main():
     import torch
     import exact_attention_26_amd as fa
     from exact_attention_26_amd import workloads as w
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+
+    # ---- host inputs: the forward bench workload and the paged decode, drawn
+    #      before the GPU is touched (the CPU baseline's worker pool is forked
+    #      from this process and reads them)
+    cfg = w.FWD_CONFIGS["fwd_b8_h16_n2048_d128"]
+    decode = not args.skip_decode and args.only in (None, "decode") and not args.probe_copy
+    with_cpu = (not args.no_cpu_baseline and args.only is None and decode
+                and not args.probe_copy)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    c1_host = w.fwd_config_inputs(cfg) if not args.probe_copy else None
+    if decode:
+        L = w.decode_layout(**w.DECODE_C4)
+        qdec_host = w.decode_q(L)
+        pools_host = [w.decode_pool(L, which, poison=False, threads=threads)
+                      for which in ("k", "v")]
+    log("host inputs ready")
+    cpu_report = oracle_res = None
+    if with_cpu:
+        log("timing the CPU oracle (forward bench and paged decode, all heads)")
+        cpu_report, oracle_res = cpu_baseline_run(cfg, c1_host, L, pools_host, qdec_host)
+        log(f"CPU oracle timed: {cpu_report['value']:.4f} TFLOP/s, "
+            f"{cpu_report['decode']['value']:.2f} GB/s on {cpu_report['cores']} cores")
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -218,7 +385,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"probe_copy_bytes_each_way": n * 4, "copies": max(1, args.steps)}))
         return
-    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
 
     def time_calls(fn):
         """Mean milliseconds of fn() over --steps calls, from HIP events recorded
@@ -244,31 +410,29 @@ def main():
             fn()
             torch.cuda.synchronize()
 
-    # ---- forward inputs ----
-    cfg = w.FWD_CONFIGS["fwd_b8_h16_n2048_d128"]
-    q, k, v = w.fwd_config_inputs(cfg)
-    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
-    del q, k, v
+    samples = {}                 # GPU results the oracle leg checks (host copies)
+
+    # ---- forward inputs on the device ----
+    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in c1_host)
+    del c1_host
     o_nc = torch.empty_like(qd)
     o_c = torch.empty_like(qd)
     lse_nc = torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
     lse_c = torch.empty_like(lse_nc)
     log("forward inputs ready")
 
-    # ---- decode inputs ----
-    decode = not args.skip_decode and args.only in (None, "decode")
+    # ---- decode inputs on the device ----
     if decode:
-        L = w.decode_layout(**w.DECODE_C4)
-        qdec = torch.from_numpy(w.decode_q(L)).to(dev).to(torch.bfloat16)
+        qdec = torch.from_numpy(qdec_host).to(dev).to(torch.bfloat16)
         pools = []
-        for which in ("k", "v"):
+        for host in pools_host:
             pool = torch.empty((L.num_blocks, L.H, L.page_size, L.d), dtype=torch.bfloat16,
                                device=dev)
-
-            def put(lo, hi, x, pool=pool):
-                pool[lo:hi].copy_(torch.from_numpy(x).to(dev))
-            w.decode_pool(L, which, poison=False, chunk_callback=put)
+            for lo in range(0, L.num_blocks, w.POOL_CHUNK_PAGES):
+                hi = min(L.num_blocks, lo + w.POOL_CHUNK_PAGES)
+                pool[lo:hi].copy_(torch.from_numpy(host[lo:hi]).to(dev))
             pools.append(pool)
+        del pools_host, host
         kc, vc = pools
         bt = torch.from_numpy(L.block_table).to(dev)
         sl = torch.from_numpy(L.seq_lens).to(dev)
@@ -362,13 +526,41 @@ def main():
                      "kernel": "fwd_bf16_kernel<128,false>",
                      "flops_per_launch": f_nc},
     }
+    # the step's last results, at the rows the oracle leg checks
+    if with_cpu:
+        rows = torch.from_numpy(_parity_rows(cfg.N)).to(dev)
+        samples["c1"] = {c: (o_.index_select(2, rows).float().cpu().numpy(),
+                             l_.index_select(2, rows).cpu().numpy())
+                         for c, (o_, l_) in ((False, (o_nc, lse_nc)), (True, (o_c, lse_c)))}
+        if run_dec:
+            samples["c4"] = (o_dec.float().cpu().numpy(), lse_dec.cpu().numpy())
     if decode:
         gbs = dec_bytes / (t_dec * 1e-3) / 1e9
+        # the same decode with 512 MiB written between calls (more than the
+        # 256 MB last-level cache), so no call finds the previous one's pages
+        # there; only the decode sits between the events
+        flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        dcall = lambda: fa.fa_paged_decode(qdec, kc, vc, bt, sl, o_dec, lse_dec, L.scale, ws)  # noqa: E731
+        warm_up(dcall)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (a, b) in enumerate(fev):
+            flush.fill_(i & 255)
+            a.record(stream)
+            dcall()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t_flushed = sum(a.elapsed_time(b) for a, b in fev) / args.steps
+        del flush
+        gbs_flushed = dec_bytes / (t_flushed * 1e-3) / 1e9
         out["decode"] = {"ms": round(t_dec, 4), "ms_median_min": med_min[2],
                          "hbm_gbs": round(gbs, 1),
                          "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes": dec_bytes, "logical_bytes": dec_logical,
-                         "logical_gbs": round(dec_logical / (t_dec * 1e-3) / 1e9, 1)}
+                         "logical_gbs": round(dec_logical / (t_dec * 1e-3) / 1e9, 1),
+                         "flushed": {"ms": round(t_flushed, 4), "hbm_gbs": round(gbs_flushed, 1),
+                                     "frac_peak": round(gbs_flushed / PEAK_HBM_GBS, 4),
+                                     "between_calls": "512 MiB device write (cache flush)"}}
         out["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs, 1),
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -513,20 +705,21 @@ def main():
 
     # ---- the other forward configurations: the sequence sweep at 16k tokens
     #      (H=32, d=64) and the long-context one (B=1 H=16 N=16384 d=128,
-    #      causal, q and k with standard deviation 3), inputs drawn on the GPU
+    #      causal, q and k with standard deviation 3), on their seeded inputs
     if not args.skip_sweep and args.only is None:
-        gen = torch.Generator(device=dev)
         out["sweep"] = {}
+        samples["sweep"] = {}
         for name, c in w.FWD_CONFIGS.items():
             if not (name.startswith("sweep_") or name.startswith("long_")):
                 continue
-            gen.manual_seed(c.seed)
-            shape = (c.B, c.H, c.N, c.d)
-            qs = (torch.randn(shape, generator=gen, device=dev) * c.sigma_qk).to(torch.bfloat16)
-            ks = (torch.randn(shape, generator=gen, device=dev) * c.sigma_qk).to(torch.bfloat16)
-            vs = (torch.randn(shape, generator=gen, device=dev) * c.sigma_v).to(torch.bfloat16)
+            host = w.fwd_config_inputs(c)
+            qs, ks, vs = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in host)
             os_ = torch.empty_like(qs)
-            ls = torch.empty(shape[:-1], dtype=torch.float32, device=dev)
+            ls = torch.empty(qs.shape[:-1], dtype=torch.float32, device=dev)
+            heads = [(0, 0), (c.B - 1, c.H - 1)]
+            prow = _parity_rows(c.N)
+            prow_d = torch.from_numpy(prow).to(dev)
+            modes = {}
             row = {}
             for causal in c.causal:
                 fn = lambda: fa.fa_fwd(qs, ks, vs, os_, ls, causal, c.scale)  # noqa: E731
@@ -536,9 +729,27 @@ def main():
                 tf = fwd_flops(c.B, c.H, c.N, c.d, causal) / (t * 1e-3) / 1e12
                 row[f"{tag}_ms"] = round(t, 4)
                 row[f"{tag}_tflops"] = round(tf, 2)
+                if with_cpu:
+                    modes[causal] = tuple(np.stack([x[b, h] for b, h in heads]) for x in host) + (
+                        np.stack([os_[b, h].index_select(0, prow_d).float().cpu().numpy()
+                                  for b, h in heads]),
+                        np.stack([ls[b, h].index_select(0, prow_d).cpu().numpy()
+                                  for b, h in heads]))
             out["sweep"][f"B={c.B} H={c.H} N={c.N} d={c.d}"] = row
-            del qs, ks, vs, os_, ls
+            if with_cpu:
+                samples["sweep"][f"B={c.B} H={c.H} N={c.N} d={c.d}"] = (c, heads, prow, modes)
+            del qs, ks, vs, os_, ls, host
         log("sweep timed")
+
+    # ---- the fp32 smoke configuration (B=1 H=2 N=256 d=64), checked in full
+    if with_cpu:
+        c0 = w.FWD_CONFIGS["smoke"]
+        h0 = w.fwd_config_inputs(c0)
+        o0, l0 = fa.attention(*(torch.from_numpy(x).to(dev) for x in h0), causal=False,
+                              scale=c0.scale)
+        torch.cuda.synchronize()
+        samples["smoke"] = ((h0[0][0], h0[1][0], h0[2][0], c0.scale),
+                            (o0[0].cpu().numpy(), l0[0].cpu().numpy()))
 
     # ---- context: the MFMA throughput a plain bf16 GEMM reaches through the
     #      vendor BLAS (torch.matmul -> hipBLASLt) on the same GPU, same clocks
@@ -616,9 +827,13 @@ def main():
               "prefill": t_pre, "tree": t_tree, "rope": t_rope, "gemm": t_gemm}[args.only]
         print(json.dumps({"only": args.only, "ms": ms}), flush=True)
         return
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline()
+    if with_cpu:
+        log("checking the GPU results against the oracle")
+        out["cpu_baseline"] = cpu_report
+        out["parity"] = cpu_baseline_parity(samples, oracle_res, L)
+        cpu_report["gpu_speedup"] = {
+            "fwd": round(value / cpu_report["value"], 1),
+            "decode": round(gbs / cpu_report["decode"]["value"], 1)}
     print(json.dumps(out), flush=True)
 
 

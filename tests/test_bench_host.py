@@ -16,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _bench():
     spec = importlib.util.spec_from_file_location("bench_host", os.path.join(ROOT, "bench.py"))
     mod = importlib.util.module_from_spec(spec)
+    sys.modules["bench_host"] = mod      # the oracle leg's forked workers look it up by name
     spec.loader.exec_module(mod)
     return mod
 
@@ -89,3 +90,37 @@ def test_decode_bytes_count_distinct_rows_once():
     alg, logi = b.decode_bytes(L)
     assert alg == len(rows) * L.H * L.d * 4 + small
     assert logi == logical * L.H * L.d * 4 + small
+
+
+def test_cpu_baseline_leg_on_a_small_workload():
+    """The oracle leg reports the host's core count (the process's affinity),
+    the BLAS library and its thread counts, and rates for the forward and the
+    decode; the parity it reports is zero for the oracle's own values and
+    catches an error planted in one entry."""
+    b = _bench()
+    cfg = w.FwdConfig("tiny", B=1, H=2, N=300, d=64, dtype="bf16", causal=(False, True), seed=5)
+    c1 = w.fwd_config_inputs(cfg)
+    L = w.decode_layout(6, S=3, H=2, d=64, lens=[1, 40, 300], shared_prefix=32, spare=2,
+                        len_range=(1, 300))
+    pools = [w.decode_pool(L, "k"), w.decode_pool(L, "v")]
+    qd = w.decode_q(L)
+    report, oracle = b.cpu_baseline_run(cfg, c1, L, pools, qd)
+    assert report["cores"] == len(os.sched_getaffinity(0))
+    assert report["workers"] == report["cores"] and report["blas_threads_per_worker"] == 1
+    assert "blas_threads_in_parent" in report and isinstance(report["blas"], str)
+    assert report["kind"] == "oracle" and report["value"] > 0 and report["decode"]["value"] > 0
+    rows = b._parity_rows(cfg.N)
+    o = {c: np.zeros((cfg.B, cfg.H, rows.size, cfg.d)) for c in (False, True)}
+    lse = {c: np.zeros((cfg.B, cfg.H, rows.size)) for c in (False, True)}
+    for (c, bb, h), (ro, rl) in oracle["c1"].items():
+        o[c][bb, h], lse[c][bb, h] = ro, rl
+    samples = {"c1": {c: (o[c], lse[c]) for c in (False, True)},
+               "c4": (oracle["c4"][0].copy(), oracle["c4"][1].copy())}
+    par = b.cpu_baseline_parity(samples, oracle, L)
+    assert all(v["o_max_abs"] == 0.0 and v["lse_max_abs"] == 0.0 for v in par.values()), par
+    samples["c4"][0][1, 1, 3] += 0.25
+    o[True][0, 1, 2, 5] -= 0.5
+    par = b.cpu_baseline_parity(samples, oracle, L)
+    assert par["paged decode S=64 H=32 d=128"]["o_max_abs"] == 0.25
+    assert par["fwd B=8 H=16 N=2048 d=128 causal"]["o_max_abs"] == 0.5
+    assert par["fwd B=8 H=16 N=2048 d=128 non-causal"]["o_max_abs"] == 0.0
