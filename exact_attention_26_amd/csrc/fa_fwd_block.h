@@ -198,17 +198,24 @@ constexpr int kMaxTreeNodes = 64;
 // tile maximum (in-lane, then the partner lane of the query), a rescale of
 // (O, l) only when the row maximum grows by more than the threshold (m_run
 // is the reference maximum of O and l), then p = 2^(c*s - c*m) into the bf16
-// operand of O^T += V^T P^T and the fp32 row sum.
-template <int ND>
+// operand of O^T += V^T P^T and the fp32 row sum.  The maximum and the sum
+// run as CH independent chains (CH = 1 or 2 or 4: a single chain waits on
+// each dependent result; more chains hold more registers).
+template <int ND, int CH = 2>
 __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m_run, float& l_run,
                                              f32x16 (&oacc)[ND], bf16x8 (&pop)[2][2], float c,
                                              float tau_raw) {
-    float mt = kNegInf;
+    static_assert(CH == 1 || CH == 2 || CH == 4, "chains");
+    float mq[CH];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < CH; ++i) mq[i] = sacc[0][i];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    mt = pair_max(mt);
+    for (int i = CH; i < 32; ++i) mq[i % CH] = fmaxf(mq[i % CH], sacc[i >> 4][i & 15]);
+#pragma unroll
+    for (int w = CH / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) mq[i] = fmaxf(mq[i], mq[i + w]);
+    const float mt = pair_max(mq[0]);
     if (__any(mt > m_run + tau_raw)) {
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2((m_run - m_new) * c);
@@ -220,16 +227,23 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m_run, fl
         m_run = m_new;
     }
     const float mc = (m_run == kNegInf) ? 0.f : m_run * c;
-    float ps0 = 0.f, ps1 = 0.f;
+    constexpr int CS = CH < 2 ? 2 : CH;            // partial sums
+    float ps[CS];
+#pragma unroll
+    for (int i = 0; i < CS; ++i) ps[i] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float p = fast_exp2(fmaf(sacc[kb][r], c, -mc));
-            if (r & 1) ps1 += p; else ps0 += p;
+            ps[r % CS] += p;
             pop[kb][r >> 3][r & 7] = (__bf16)p;
         }
-    l_run += ps0 + ps1;                        // row sum from the fp32 probabilities
+#pragma unroll
+    for (int w = CS / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) ps[i] += ps[i + w];
+    l_run += ps[0];                                // row sum from the fp32 probabilities
 }
 
 // S^T = K Q^T for the tile's two 32-key blocks: K fragments read from the
