@@ -80,21 +80,21 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
 }
 
-// Non-causal forward as a persistent grid: one work group per CU walks its
+// The d = 128 forward as a persistent grid: one work group per CU walks its
 // blocks of 256 query rows as one stream of key tiles (fa_fwd_persist.h).
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1)
 void fwd_bf16_persist_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                             float* __restrict__ LSE, int N, int n_qblocks, int total_blocks,
+                             float* __restrict__ LSE, int N, int n_qblocks, int total_units,
                              float scale_log2) {
     constexpr int TILE = FwdShape<D>::TILE;
     __shared__ __attribute__((aligned(1024))) uint16_t kb0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
-    fwd_pingpong_persistent<D>(kb0, kb1, vb0, vb1, Q, K, V, O, LSE, N, n_qblocks, total_blocks,
-                               scale_log2);
+    fwd_pingpong_persistent<D, CAUSAL>(kb0, kb1, vb0, vb1, Q, K, V, O, LSE, N, n_qblocks,
+                                       total_units, scale_log2);
 }
 
 // Compute units of the current device (queried once per device).
@@ -112,11 +112,11 @@ int cu_count() {
     return counts[dev];
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t launch_persist(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int H, int N, float scale, hipStream_t stream) {
     const int n_qblocks = (N + kPersistBM - 1) / kPersistBM;
-    const int total = B * H * n_qblocks;
+    const int total = B * H * units_per_head<CAUSAL>(n_qblocks);
     const int grid = total < cu_count() ? total : cu_count();
     const uint16_t* qp = static_cast<const uint16_t*>(q);
     const uint16_t* kp = static_cast<const uint16_t*>(k);
@@ -124,7 +124,7 @@ hipError_t launch_persist(const void* q, const void* k, const void* v, void* o, 
     uint16_t* op = static_cast<uint16_t*>(o);
     float scale_log2 = (float)((double)scale * 1.4426950408889634074);
     void* args[] = {&qp, &kp, &vp, &op, &lse, &N, (void*)&n_qblocks, (void*)&total, &scale_log2};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_persist_kernel<D>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_persist_kernel<D, CAUSAL>),
                            dim3(grid), dim3(512), args, 0, stream);
 }
 
@@ -151,12 +151,14 @@ hipError_t fa_launch_fwd_bf16(const void* q, const void* k, const void* v, void*
                               int B, int H, int N, int d, int causal, float scale,
                               hipStream_t stream) {
     if (d == 128) {
-        if (causal) return launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream);
         // the persistent stream has no ragged tile; short sequences (blocks
         // of few tiles) stay on the per-block grid
-        if (N % kFwdBN == 0 && N >= kPersistMinTiles * kFwdBN)
-            return launch_persist<128>(q, k, v, o, lse, B, H, N, scale, stream);
-        return launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+        const bool persist = N % kFwdBN == 0 && N >= kPersistMinTiles * kFwdBN;
+        if (causal)
+            return persist ? launch_persist<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
+                           : launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream);
+        return persist ? launch_persist<128, false>(q, k, v, o, lse, B, H, N, scale, stream)
+                       : launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
     }
     if (d == 64)
         return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, stream)

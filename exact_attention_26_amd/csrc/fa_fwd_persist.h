@@ -37,7 +37,14 @@ constexpr int kPersistBM = 256;                // query rows per block (8 waves 
 // tiles, run on the per-block grid.
 constexpr int kPersistMinTiles = 11;
 
-// Blocks of work group `wg` of `G`: i * G + slot, i = 0, 1, ...  With G a
+// Work units of a (sequence, head): a block each, or (causal) pairs of a
+// long and a short block, (n + 1) / 2 of them.
+template <bool CAUSAL>
+__host__ __device__ constexpr int units_per_head(int n_qblocks) {
+    return CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;
+}
+
+// Units of work group `wg` of `G`: i * G + slot, i = 0, 1, ...  With G a
 // multiple of 8, the work groups of one XCD (wg % 8, the hardware's
 // round-robin) take a contiguous range of G / 8 blocks in every round, so the
 // blocks of a head share that XCD's L2.
@@ -45,11 +52,11 @@ __device__ __forceinline__ int persist_slot(int wg, int G) {
     return (G & 7) == 0 ? (wg & 7) * (G >> 3) + (wg >> 3) : wg;
 }
 
-template <int D>
+template <int D, bool CAUSAL, int AHEAD = 4>
 __device__ __forceinline__ void fwd_pingpong_persistent(
     uint16_t* kb0, uint16_t* kb1, uint16_t* vb0, uint16_t* vb1,
     const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O, float* LSE, int N,
-    int n_qblocks, int total_blocks, float scale_log2) {
+    int n_qblocks, int total_units, float scale_log2) {
     constexpr int W = 8;
     constexpr int BM = kPersistBM;
     using Sh = FwdShape<D, W>;
@@ -67,36 +74,73 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
     const uint32_t qflip = (scale_log2 < 0.f) ? 0x80008000u : 0u;
     const float tau_raw = (c > 0.f) ? kRescaleThreshold / c : __builtin_inff();
 
-    const int n_kt = N / kFwdBN;                   // N % 64 == 0, n_kt >= kPersistMinTiles
-    const int bytes = N * D * 2;
+    const int bytes = N * D * 2;                   // N % 64 == 0
     const int G = gridDim.x;
     const int slot = persist_slot(blockIdx.x, G);
-    const int nb = (slot < total_blocks) ? (total_blocks - slot + G - 1) / G : 0;
-    if (nb == 0) return;
-    const int T = nb * n_kt;                       // tiles of the stream
-
-    // block i of this work group: its (b, h) and first query row
-    auto bh_of = [&](int i) __attribute__((always_inline)) { return (i * G + slot) / n_qblocks; };
-    auto q0_of = [&](int i) __attribute__((always_inline)) {
-        const int b = i * G + slot;
-        return (b - (b / n_qblocks) * n_qblocks) * BM;
+    // work units: non-causal, one block; causal, blocks n_qblocks-1-p and p of
+    // a head (one block when they coincide), about the same number of key
+    // tiles for every unit.  Unit j of this work group is u = j * G + slot.
+    const int per_head = units_per_head<CAUSAL>(n_qblocks);
+    const int nu = (slot < total_units) ? (total_units - slot + G - 1) / G : 0;
+    if (nu == 0) return;
+    // key tiles of query block qb: all of them, or (causal) those up to its
+    // last row
+    auto tiles_of = [&](int qb) __attribute__((always_inline)) {
+        return (CAUSAL ? min(N, (qb + 1) * BM) : N) / kFwdBN;
     };
-    // a tile's place in the stream, advanced one tile per iteration (no
-    // divisions in the loop: on this target an integer division is a long
-    // sequence of vector instructions)
+    // a tile's place in the stream, advanced one tile per iteration
     struct Pos {
-        int blk;                                   // block (nb when past the end)
+        int j;                                     // unit (nu when past the end)
+        int m;                                     // block of the unit (causal: 0 long, 1 short)
         int kt;                                    // key tile of the block
-        size_t head;                               // element offset of the block's (b, h)
+        int n_kt;                                  // key tiles of the block
+        int q0;                                    // first query row of the block
+        int bh;                                    // (b, h) of the block
+    };
+    // the block of p.j / p.m (past the end: tile 0, 1, ... of head 0, in bounds)
+    auto set_block = [&](Pos& p) __attribute__((always_inline)) {
+        if (p.j < nu) {
+            const int u = p.j * G + slot;
+            const int bh = u / per_head;
+            const int pp = u - bh * per_head;
+            const int qb = (CAUSAL && p.m == 0) ? n_qblocks - 1 - pp : pp;
+            p.bh = bh;
+            p.q0 = qb * BM;
+            p.n_kt = tiles_of(qb);
+        } else {
+            p.bh = 0;
+            p.q0 = 0;
+            p.n_kt = 1 << 30;
+        }
     };
     auto advance = [&](Pos p) __attribute__((always_inline)) {
-        if (++p.kt == n_kt) {
+        if (++p.kt == p.n_kt) {
             p.kt = 0;
-            ++p.blk;
-            p.head = (p.blk < nb) ? (size_t)bh_of(p.blk) * N * D : 0;
+            const int pp = (p.j * G + slot) % per_head;
+            if (CAUSAL && p.m == 0 && 2 * pp != n_qblocks - 1) {
+                p.m = 1;                           // the short block of the pair
+            } else {
+                p.m = 0;
+                ++p.j;
+            }
+            set_block(p);
         }
         return p;
     };
+    auto head_of = [&](const Pos& p) __attribute__((always_inline)) {
+        return (size_t)p.bh * N * D;
+    };
+    // tiles of the stream
+    int T = 0;
+    for (int j = 0; j < nu; ++j) {
+        const int pp = (j * G + slot) % per_head;
+        if (CAUSAL) {
+            T += tiles_of(n_qblocks - 1 - pp);
+            if (2 * pp != n_qblocks - 1) T += tiles_of(pp);
+        } else {
+            T += tiles_of(pp);
+        }
+    }
 
     // the K and V tiles are loaded by the four waves of the first group
     // alone (2 * LPW regions of each per wave), inside their matrix phase:
@@ -108,31 +152,33 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
     // the tile at `p` (K or V) into LDS `dst`
     auto load_kv = [&](const uint16_t* X, const Pos& p, uint16_t* dst)
                        __attribute__((always_inline)) {
-        load_tile_lds<LPW4>(X + p.head, bytes, p.kt * kFwdBN * D * 2, &gofs[0], dst,
+        load_tile_lds<LPW4>(X + head_of(p), bytes, p.kt * kFwdBN * D * 2, &gofs[0], dst,
                             (wave & 3) * LPW4);
     };
     bf16x8 qop[NKC];
-    // the next block's query fragments for this lane, raw (the sign of a
-    // negative scale and rows past N are applied when that block starts),
-    // into the registers of this block's, dead after its last score MFMAs
-    auto load_q_next = [&](int i) __attribute__((always_inline)) {
-        const int row = min(q0_of(i) + wave * 32 + l32, N - 1);
-        const uint16_t* qr = Q + (size_t)bh_of(i) * N * D + (size_t)row * D + g * 8;
+    // the query fragments for this lane of the block at `p`, raw (the sign of
+    // a negative scale and rows past N are applied when that block starts),
+    // into the registers of the block before, dead after its last scores
+    auto load_q_next = [&](const Pos& p) __attribute__((always_inline)) {
+        const int row = min(p.q0 + wave * 32 + l32, N - 1);
+        const uint16_t* qr = Q + head_of(p) + (size_t)row * D + g * 8;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
             qop[kc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + kc * 16));
     };
 
     // ---- the first block: K_0 in flight during its query loads
-    Pos cur{0, 0, (size_t)bh_of(0) * N * D};       // tile k of iteration k
+    Pos cur{0, 0, 0, 0, 0, 0};                     // tile k of iteration k
+    set_block(cur);
+    Pos prv = cur;                                 // tile k - 1
     Pos nxt = advance(cur);                        // tile k + 1
     load_kv(K, cur, kb0);
     {
         QRows qr0;
-        qr0.Q = Q + cur.head;
+        qr0.Q = Q + head_of(cur);
         qr0.stride = D;
         qr0.rows = N;
-        load_q_operand<D, false>(qr0, q0_of(0) + wave * 32 + l32, g, qflip, qop);
+        load_q_operand<D, false>(qr0, cur.q0 + wave * 32 + l32, g, qflip, qop);
     }
 
     f32x16 oacc[ND];
@@ -155,9 +201,9 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
     bf16x8 pop[2][2];
 
     // finish block i: O = O_acc / l, LSE = m + ln l (as in fwd_block)
-    auto finish = [&](int i) __attribute__((always_inline)) {
-        const int row = q0_of(i) + wave * 32 + l32;
-        const size_t bh = (size_t)bh_of(i);
+    auto finish = [&](const Pos& p) __attribute__((always_inline)) {
+        const int row = p.q0 + wave * 32 + l32;
+        const size_t bh = (size_t)p.bh;
         const float l_tot = pair_sum(l_run);
         if (row < N) {
             const bool empty = !(l_tot > 0.f);
@@ -208,6 +254,7 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
     };
     constexpr int kPV = 4 * ND;                    // PV products per tile (two reads each)
     constexpr int kS = 2 * NKC;                    // score products per tile (one read each)
+    constexpr int kAhead = AHEAD;                  // MFMAs whose operands are read ahead
 
     // M(k) of a middle iteration, one stream of MFMAs: PV of tile k-1 with
     // four operands (eight transposing reads) in flight, the first four K
@@ -218,9 +265,9 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
                         uint16_t* vcur) __attribute__((always_inline)) {
         constexpr bool LD = decltype(with_loads)::value;
         const bool boundary = cur.kt == 0;
-        if (boundary && (qflip != 0u || q0_of(cur.blk) + BM > N)) {
+        if (boundary && (qflip != 0u || cur.q0 + BM > N)) {
             // rare: a negative scale, or rows past N in the new block
-            const uint32_t keep = (q0_of(cur.blk) + wave * 32 + l32 < N) ? 0xFFFFFFFFu : 0u;
+            const uint32_t keep = (cur.q0 + wave * 32 + l32 < N) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
                 qop[kc] = __builtin_bit_cast(
@@ -237,24 +284,27 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
             load_kv(K, nxt, knext);
             load_kv(V, cur, vcur);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // reads for MFMA j + kAhead issued right after MFMA j (two per PV
+        // product, one per score product); the eight tile loads after PV
+        // products 1, 4, 7 and 10
+        // (the builtin takes constants only: the branches fold away once the
+        // loops are unrolled)
 #pragma unroll
-        for (int i = 0; i < kPV - 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            // the eight tile loads, two after every third PV product
-            if (LD && i % 3 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        for (int j = 0; j < kAhead; ++j) {
+            if (j < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4 + kS - 4; ++i) {
+        for (int j = 0; j < kPV + kS; ++j) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (j + kAhead < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else if (j + kAhead < kPV + kS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (LD && j < 12 && j % 3 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (boundary) {
-            finish(cur.blk - 1);
+            finish(prv);
 #pragma unroll
             for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -262,7 +312,7 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
             m_run = kNegInf;
             l_run = 0.f;
         }
-        if (cur.kt == n_kt - 1 && cur.blk + 1 < nb) load_q_next(cur.blk + 1);
+        if (cur.kt == cur.n_kt - 1 && nxt.j < nu) load_q_next(nxt);
     };
     // M(0): the scores of the first tile only
     auto m_first = [&](const uint16_t* ks) __attribute__((always_inline)) {
@@ -286,9 +336,34 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
-    // V: online softmax of the scores just computed (every key of every tile
-    // exists: N is a multiple of the tile)
-    auto v_phase = [&]() __attribute__((always_inline)) {
+    // V: online softmax of the scores of the tile at `t` (non-causal: every
+    // key of every tile exists, N being a multiple of the tile).  Causal: on
+    // a tile that reaches past this wave's first row, key k0 + off of the
+    // lane's row is hidden when off > row - k0, off = 32kb + 8(r/4) + 4g +
+    // r%4 for sacc[kb][r].  The mask is arithmetic, min(s, +-inf) with the
+    // sign of lim - off: no compare results to keep in scalar registers.
+    auto v_phase = [&](const Pos& t) __attribute__((always_inline)) {
+        if constexpr (CAUSAL) {
+            const int k0 = t.kt * kFwdBN;
+            if (k0 + kFwdBN - 1 > t.q0 + wave * 32) {
+                const int lim = (t.q0 + wave * 32 + l32) - (k0 + 4 * g);
+                const uint32_t sign = 0x80000000u, inf = 0x7f800000u;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        // s = min(s, +inf or, when lim - off < 0, -inf): the
+                        // bound from the sign bit, then the minimum, in one
+                        // block the compiler cannot rewrite into a select
+                        float out;
+                        asm("v_and_or_b32 %0, %1, %2, %3\n\tv_min_f32 %0, %4, %0"
+                            : "=&v"(out)
+                            : "v"(lim - off), "v"(sign), "v"(inf), "v"(sacc[kb][r]));
+                        sacc[kb][r] = out;
+                    }
+            }
+        }
         softmax_tile<ND, 2>(sacc, m_run, l_run, oacc, pop, c, tau_raw);
         // the probabilities and the row sum exist here: without this use the
         // compiler may sink their arithmetic into the next matrix phase,
@@ -323,12 +398,12 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
             load_kv(V, cur, vcur);
         }
         if constexpr (!B) m_phase();
-        else if constexpr (ST != 0) v_phase();    // softmax of tile k-1
+        else if constexpr (ST != 0) v_phase(prv);  // softmax of tile k-1
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();              // half an iteration: the groups swap units
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!B) {
-            if constexpr (ST != 2) v_phase();      // softmax of tile k
+            if constexpr (ST != 2) v_phase(cur);   // softmax of tile k
         } else {
             m_phase();
         }
@@ -338,8 +413,11 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
         // second group issues no tile loads; its query loads (issued at the
         // end of its matrix phase) stay in flight into the next iteration.
         if constexpr (!B) __builtin_amdgcn_s_waitcnt(0x0F70);
-        cur = nxt;
-        nxt = advance(nxt);
+        if constexpr (ST != 2) {                   // after the last one prv stays tile T-1
+            prv = cur;
+            cur = nxt;
+            nxt = advance(nxt);
+        }
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -361,7 +439,7 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
     };
     if (wave < 4) run(std::integral_constant<bool, false>{});
     else run(std::integral_constant<bool, true>{});
-    finish(nb - 1);
+    finish(prv);                                   // the block of the last tile
 }
 
 }  // namespace fa_gfx950

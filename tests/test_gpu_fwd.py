@@ -192,27 +192,31 @@ def test_long_sequence_sampled_rows(gpu_device, causal):
 @pytest.mark.parametrize("shape", [(12, 16, 704), (3, 100, 1024), (2, 8, 1088), (3, 100, 1000),
                                    (64, 16, 200)])
 @pytest.mark.parametrize("scale_sign", [1.0, -1.0])
-def test_many_blocks_per_work_group(gpu_device, shape, scale_sign):
-    """The persistent non-causal d=128 grid (N a multiple of 64, at least
-    eleven key tiles): 576 blocks of 256 rows for N = 704 (2.25 blocks per
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_blocks_per_work_group(gpu_device, shape, scale_sign, causal):
+    """The persistent d=128 grid (N a multiple of 64, at least eleven key
+    tiles).  Non-causal: 576 blocks of 256 rows for N = 704 (2.25 blocks per
     work group, every third block with rows past N), 1200 full blocks for
     N = 1024, and 80 blocks for N = 1088 (fewer blocks than compute units,
-    the last block of a head holding 64 rows).  A ragged N = 1000 and a short
-    N = 200 run on the per-block grid.  Sampled heads against the oracle,
-    both signs of the scale (a negative one flips the query operand at each
-    block start)."""
+    the last block of a head holding 64 rows).  Causal: units of a long and a
+    short block of one head, and a lone middle block when a head has an odd
+    number of blocks (N = 704: blocks 2+0 and 1, of 11+4 and 8 key tiles;
+    N = 1088: 4+0, 3+1 and 2, the long block of the first unit holding 64
+    rows).  A ragged N = 1000 and a short N = 200 run on the per-block grid.
+    Sampled heads against the oracle, both signs of the scale (a negative
+    one flips the query operand at each block start)."""
     B, H, N = shape
     d = 128
     q, k, v = w.fwd_inputs(B, H, N, d, seed=900 + N)
     scale = scale_sign / math.sqrt(d)
-    say(f"fwd many blocks B={B} H={H} N={N} d={d} scale={scale:+.4f}")
-    o, lse = _run(q, k, v, "bf16", False, scale, gpu_device)
+    say(f"fwd many blocks B={B} H={H} N={N} d={d} causal={causal} scale={scale:+.4f}")
+    o, lse = _run(q, k, v, "bf16", causal, scale, gpu_device)
     rng = np.random.default_rng(N)
     heads = [(0, 0), (0, H - 1), (B // 2, H // 2), (B - 1, H - 1),
              (int(rng.integers(B)), int(rng.integers(H)))]
     for b, h in heads:
         rows = sample_rows(N, rng, extra=24)
-        ro, rl = attention_fp64(q[b, h], k[b, h], v[b, h], causal=False, scale=scale, rows=rows)
+        ro, rl = attention_fp64(q[b, h], k[b, h], v[b, h], causal=causal, scale=scale, rows=rows)
         assert_close(f"o b={b} h={h}", o[b, h, rows], ro, O_ATOL["bf16"])
         assert_close(f"lse b={b} h={h}", lse[b, h, rows], rl, LSE_ATOL["bf16"])
 
