@@ -518,12 +518,16 @@ def main():
                 "noncausal_ms_median_min": med_min[0] if run_nc else None,
                 "causal_ms": round(t_c, 4), "causal_tflops": round(tflops_c, 2),
                 "causal_frac_peak": round(tflops_c / PEAK_BF16_TFLOPS, 4),
-                "causal_ms_median_min": med_min[1] if run_c else None},
+                "causal_ms_median_min": med_min[1] if run_c else None,
+                "causal_traffic": measured_traffic(
+                    "fwd_bf16_persist_kernel<128,true> B=8 H=16 N=2048"),
+                "kernels": "fwd_bf16_persist_kernel<128,false>, <128,true>"},
         "roofline": {"bound": "mfma", "achieved": round(tflops_nc, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops_nc / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("fwd_bf16_kernel<128,false> B=8 H=16 N=2048"),
-                     "kernel": "fwd_bf16_kernel<128,false>",
+                     "traffic": measured_traffic(
+                         "fwd_bf16_persist_kernel<128,false> B=8 H=16 N=2048"),
+                     "kernel": "fwd_bf16_persist_kernel<128,false>",
                      "flops_per_launch": f_nc},
     }
     # the step's last results, at the rows the oracle leg checks
