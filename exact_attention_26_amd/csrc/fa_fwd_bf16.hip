@@ -93,12 +93,14 @@ void fwd_bf16_persist_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
-    fwd_pingpong_persistent<D, CAUSAL>(kb0, kb1, vb0, vb1, Q, K, V, O, LSE, N, n_qblocks,
-                                       total_units, scale_log2);
+    fwd_pingpong_persistent<D, CAUSAL, false>(kb0, kb1, vb0, vb1, Q, K, V, O, LSE, N,
+                                              n_qblocks, total_units, scale_log2);
 }
 
+}  // namespace
+
 // Compute units of the current device (queried once per device).
-int cu_count() {
+int fa_cu_count() {
     static int counts[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -112,12 +114,14 @@ int cu_count() {
     return counts[dev];
 }
 
+namespace {
+
 template <int D, bool CAUSAL>
 hipError_t launch_persist(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int H, int N, float scale, hipStream_t stream) {
     const int n_qblocks = (N + kPersistBM - 1) / kPersistBM;
     const int total = B * H * units_per_head<CAUSAL>(n_qblocks);
-    const int grid = total < cu_count() ? total : cu_count();
+    const int grid = total < fa_cu_count() ? total : fa_cu_count();
     const uint16_t* qp = static_cast<const uint16_t*>(q);
     const uint16_t* kp = static_cast<const uint16_t*>(k);
     const uint16_t* vp = static_cast<const uint16_t*>(v);

@@ -52,11 +52,14 @@ __device__ __forceinline__ int persist_slot(int wg, int G) {
     return (G & 7) == 0 ? (wg & 7) * (G >> 3) + (wg >> 3) : wg;
 }
 
-template <int D, bool CAUSAL, int AHEAD = 4>
+// ROPE: the query rows are rotated (rotate_pairs, the angle of the row's
+// position in its head) when their block starts; K arrives rotated.
+template <int D, bool CAUSAL, bool ROPE = false, int AHEAD = 4>
 __device__ __forceinline__ void fwd_pingpong_persistent(
     uint16_t* kb0, uint16_t* kb1, uint16_t* vb0, uint16_t* vb1,
     const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O, float* LSE, int N,
-    int n_qblocks, int total_units, float scale_log2) {
+    int n_qblocks, int total_units, float scale_log2, const float* rope_cos = nullptr,
+    const float* rope_sin = nullptr) {
     constexpr int W = 8;
     constexpr int BM = kPersistBM;
     using Sh = FwdShape<D, W>;
@@ -178,7 +181,10 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
         qr0.Q = Q + head_of(cur);
         qr0.stride = D;
         qr0.rows = N;
-        load_q_operand<D, false>(qr0, cur.q0 + wave * 32 + l32, g, qflip, qop);
+        qr0.rope_cos = rope_cos;
+        qr0.rope_sin = rope_sin;
+        qr0.pos0 = 0;
+        load_q_operand<D, ROPE>(qr0, cur.q0 + wave * 32 + l32, g, qflip, qop);
     }
 
     f32x16 oacc[ND];
@@ -265,13 +271,29 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
                         uint16_t* vcur) __attribute__((always_inline)) {
         constexpr bool LD = decltype(with_loads)::value;
         const bool boundary = cur.kt == 0;
-        if (boundary && (qflip != 0u || cur.q0 + BM > N)) {
-            // rare: a negative scale, or rows past N in the new block
-            const uint32_t keep = (cur.q0 + wave * 32 + l32 < N) ? 0xFFFFFFFFu : 0u;
+        if (boundary && (ROPE || qflip != 0u || cur.q0 + BM > N)) {
+            // rare: the rotation, a negative scale, or rows past N in the new
+            // block (the rows were loaded from min(row, N - 1))
+            const int row = cur.q0 + wave * 32 + l32;
+            const uint32_t keep = (row < N) ? 0xFFFFFFFFu : 0u;
+            u32x4 xq[NKC];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) xq[kc] = __builtin_bit_cast(u32x4, qop[kc]);
+            if constexpr (ROPE) {
+                // elements kc*16 + 8g .. +8 are pairs kc*8 + 4g .. +4
+                const int64_t t0 = (int64_t)min(row, N - 1) * (D / 2) + g * 4;
+                float4 cq[NKC], sq[NKC];
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    cq[kc] = *reinterpret_cast<const float4*>(rope_cos + t0 + kc * 8);
+                    sq[kc] = *reinterpret_cast<const float4*>(rope_sin + t0 + kc * 8);
+                }
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) xq[kc] = rotate_pairs(xq[kc], cq[kc], sq[kc]);
+            }
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
-                qop[kc] = __builtin_bit_cast(
-                    bf16x8, (__builtin_bit_cast(u32x4, qop[kc]) & keep) ^ qflip);
+                qop[kc] = __builtin_bit_cast(bf16x8, (xq[kc] & keep) ^ qflip);
         }
         __builtin_amdgcn_sched_barrier(0);
         // the matrix wave of each SIMD issues first when both waves are ready:

@@ -9,6 +9,10 @@ hipError_t fa_launch_fwd(const void* q, const void* k, const void* v, void* o, f
                          int B, int H, int N, int d, int causal, float scale, int dtype,
                          hipStream_t stream);
 
+// Compute units of the current device, queried once per device (fa_fwd_bf16.hip):
+// the grid of the persistent forwards
+int fa_cu_count();
+
 // bf16 fast path (fa_fwd_bf16.hip)
 hipError_t fa_launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                               int B, int H, int N, int d, int causal, float scale,

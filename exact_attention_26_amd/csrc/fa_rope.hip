@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include "fa_fwd_block.h"
+#include "fa_fwd_persist.h"
 #include "fa_kernels.h"
 
 namespace {
@@ -98,6 +99,25 @@ void fwd_rope_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
 }
 
+// The d = 128 forward with the query rotation fused, as the persistent stream
+// (fa_fwd_persist.h): each block's query rows are rotated in registers when
+// the block starts.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1)
+void fwd_rope_persist_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                             const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                             float* __restrict__ LSE, const float* __restrict__ rope_cos,
+                             const float* __restrict__ rope_sin, int N, int n_qblocks,
+                             int total_units, float scale_log2) {
+    constexpr int TILE = FwdShape<D>::TILE;
+    __shared__ __attribute__((aligned(1024))) uint16_t kb0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
+    fwd_pingpong_persistent<D, CAUSAL, true>(kb0, kb1, vb0, vb1, Q, K, V, O, LSE, N, n_qblocks,
+                                             total_units, scale_log2, rope_cos, rope_sin);
+}
+
 template <int D>
 hipError_t launch_rope(const void* x, void* y, const float* c, const float* s, int64_t rows,
                        int n, hipStream_t stream) {
@@ -107,6 +127,24 @@ hipError_t launch_rope(const void* x, void* y, const float* c, const float* s, i
     void* args[] = {&xp, &yp, (void*)&c, (void*)&s, &chunks, &n};
     return hipLaunchKernel(reinterpret_cast<const void*>(&rope_kernel<D>),
                            dim3((unsigned)((chunks + 255) / 256)), dim3(256), args, 0, stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_persist(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const float* c, const float* s, int B, int H, int N, float scale,
+                              hipStream_t stream) {
+    const int n_qblocks = (N + kPersistBM - 1) / kPersistBM;
+    const int total = B * H * units_per_head<CAUSAL>(n_qblocks);
+    const int grid = total < fa_cu_count() ? total : fa_cu_count();
+    const uint16_t* qp = static_cast<const uint16_t*>(q);
+    const uint16_t* kp = static_cast<const uint16_t*>(k);
+    const uint16_t* vp = static_cast<const uint16_t*>(v);
+    uint16_t* op = static_cast<uint16_t*>(o);
+    float scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    void* args[] = {&qp, &kp, &vp, &op, &lse, (void*)&c, (void*)&s, &N, (void*)&n_qblocks,
+                    (void*)&total, &scale_log2};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_rope_persist_kernel<D, CAUSAL>),
+                           dim3(grid), dim3(512), args, 0, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -144,11 +182,19 @@ hipError_t fa_launch_fwd_rope(const void* q, const void* k, const void* v, void*
                               hipStream_t stream) {
     hipError_t e = fa_launch_rope(k, workspace, rope_cos, rope_sin, B, H, N, d, stream);
     if (e != hipSuccess) return e;
-    if (d == 128)
+    if (d == 128) {
+        // the persistent stream as in the plain forward (no ragged tile; short
+        // sequences stay on the per-block grid)
+        if (N % kFwdBN == 0 && N >= kPersistMinTiles * kFwdBN)
+            return causal ? launch_fwd_persist<128, true>(q, workspace, v, o, lse, rope_cos,
+                                                          rope_sin, B, H, N, scale, stream)
+                          : launch_fwd_persist<128, false>(q, workspace, v, o, lse, rope_cos,
+                                                           rope_sin, B, H, N, scale, stream);
         return causal ? launch_fwd<128, true>(q, workspace, v, o, lse, rope_cos, rope_sin, B, H,
                                               N, scale, stream)
                       : launch_fwd<128, false>(q, workspace, v, o, lse, rope_cos, rope_sin, B, H,
                                                N, scale, stream);
+    }
     if (d == 64)
         return causal ? launch_fwd<64, true>(q, workspace, v, o, lse, rope_cos, rope_sin, B, H,
                                              N, scale, stream)
