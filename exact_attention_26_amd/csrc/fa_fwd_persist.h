@@ -11,7 +11,9 @@
 // Tile t of the stream is tile t % n_kt of block t / n_kt.  Iteration k:
 // the first group's matrix phase (PV of tile k-1, then the scores of tile k,
 // one stream of 32 MFMAs) while the second group runs the softmax of tile
-// k-1; then the groups swap.  What differs from one block per work group:
+// k-1; then the groups swap (one barrier per iteration, at its top: the
+// groups keep the offset between their phases by themselves).  What differs
+// from one block per work group:
 //  - no block start or end stalls the CU: at a block boundary the matrix
 //    phase computes the new block's first scores right after the old block's
 //    last PV, then finishes the old block (normalise, store O and LSE: the
@@ -421,8 +423,10 @@ __device__ __forceinline__ void fwd_pingpong_persistent(
         }
         if constexpr (!B) m_phase();
         else if constexpr (ST != 0) v_phase(prv);  // softmax of tile k-1
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();              // half an iteration: the groups swap units
+        // no barrier between the halves: the top barrier orders every reuse of
+        // an LDS buffer, and the groups keep their half-iteration offset by
+        // themselves (A starts with its MFMAs, B with its softmax, and the
+        // MFMA wave of a SIMD issues first): a barrier here cost 1.5-2.5 %
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!B) {
             if constexpr (ST != 2) v_phase(cur);   // softmax of tile k
