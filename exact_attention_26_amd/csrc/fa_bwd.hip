@@ -162,9 +162,14 @@ __device__ __forceinline__ void dkdv1_block(uint16_t* smem0, uint16_t* smem1,
         load_tile_lds<LPW>(Qh, bytes, tb, &gofs[0], stage, wave * LPW);
         load_tile_lds<LPW>(dOh, bytes, tb, &gofs[0], stage + TILE, wave * LPW);
         // the two 32-row statistics blocks of the tile (and 512 bytes more,
-        // unused; zeros past the end of the head's statistics)
-        if (wave == 0) load_kib_lds(st_h, n_sb * SB_FLOATS * 4, qt * 2 * SB_FLOATS * 4,
-                                    stage + 2 * TILE, lane);
+        // unused), the offset in the range-checked per-lane part: zeros past
+        // the end of the head's statistics
+        if (wave == 0) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)st_h, (short)0, n_sb * SB_FLOATS * 4, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + 2 * TILE), 16,
+                                                     qt * 2 * SB_FLOATS * 4 + lane * 16, 0, 0, 0);
+        }
     };
 
     int rofs[NKC];                             // row-major fragment: query row l32, chunk 2kc+g

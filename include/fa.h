@@ -115,7 +115,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 /*
  * fa_bwd_workspace_size - bytes of device workspace fa_bwd needs for these
  * sizes (0 if the sizes are invalid).  Host-only, no HIP call.  It is
- * B * H * ceil(N / 64) KiB: per 64 rows, their log-sum-exp and dO . O.
+ * B * H * ceil(N / 32) * 256 bytes: per 32 rows, their log-sum-exp and dO . O.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 

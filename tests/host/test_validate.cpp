@@ -97,9 +97,9 @@ int main() {
     EXPECT_EQ(check_decode(p, p, p, p, p, p, 64, 32, 128, 16, 512, 17874, 0.1f, FA_F32, p, ws),
               FA_ERR_UNSUPPORTED);
 
-    // backward workspace: one KiB per 64 rows of every head
-    EXPECT_EQ(bwd_workspace_bytes(8, 16, 2048, 128), 8ull * 16 * 32 * 1024);
-    EXPECT_EQ(bwd_workspace_bytes(1, 1, 65, 64), 2ull * 1024);
+    // backward workspace: 256 bytes per 32 rows of every head
+    EXPECT_EQ(bwd_workspace_bytes(8, 16, 2048, 128), 8ull * 16 * 64 * 256);
+    EXPECT_EQ(bwd_workspace_bytes(1, 1, 65, 64), 3ull * 256);
     EXPECT_EQ(bwd_workspace_bytes(1, 1, 0, 64), 0);
     const size_t bws = bwd_workspace_bytes(8, 16, 2048, 128);
     // backward: valid

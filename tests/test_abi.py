@@ -86,9 +86,9 @@ def test_fwd_rejects_before_launch(kw, status):
 
 
 def test_bwd_workspace_size():
-    # one KiB per 64 rows of every head
-    assert fa.fa_bwd_workspace_size(8, 16, 2048, 128) == 8 * 16 * 32 * 1024
-    assert fa.fa_bwd_workspace_size(1, 2, 65, 64) == 2 * 2 * 1024
+    # 256 bytes per 32 rows of every head
+    assert fa.fa_bwd_workspace_size(8, 16, 2048, 128) == 8 * 16 * 64 * 256
+    assert fa.fa_bwd_workspace_size(1, 2, 65, 64) == 2 * 3 * 256
     assert fa.fa_bwd_workspace_size(1, 1, 0, 64) == 0
 
 
@@ -106,7 +106,7 @@ def _bwd(**kw):
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
     (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
     (dict(dv=None), 1), (dict(B=0), 1), (dict(N=0), 1), (dict(causal=2), 1),
-    (dict(scale=float("inf")), 1), (dict(ws=None), 1), (dict(wsb=1023), 1),
+    (dict(scale=float("inf")), 1), (dict(ws=None), 1), (dict(wsb=255), 1),
     (dict(d=96), 2), (dict(dtype=fa.FA_F32), 2), (dict(dtype=7), 2),
 ])
 def test_bwd_rejects_before_launch(kw, status):
