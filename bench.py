@@ -69,6 +69,19 @@ def fwd_flops(B, H, N, d, causal):
     return 2.0 * B * H * d * N * (N + 1) if causal else 4.0 * B * H * N * N * d
 
 
+def fwd_bytes(B, H, N, d):
+    """Algorithmic HBM bytes of a bf16 forward: q, k, v read once, o written
+    once (2 bytes each), and the fp32 log-sum-exp of every row."""
+    return B * H * N * (4 * d * 2 + 4)
+
+
+def fwd_roof_tflops(B, H, N, d, causal):
+    """The forward's roofline: the bf16 matrix peak, or the HBM rate times the
+    FLOPs per algorithmic byte when that is lower (short causal sequences)."""
+    intensity = fwd_flops(B, H, N, d, causal) / fwd_bytes(B, H, N, d)
+    return min(PEAK_BF16_TFLOPS, PEAK_HBM_GBS * 1e9 * intensity / 1e12)
+
+
 def bwd_flops(B, H, N, d, causal):
     """Algorithmic backward FLOPs: the five N x N x d products of the gradient
     (S recomputed, dP, dV, dQ, dK), 2.5x the forward's.  The dK/dV and dQ
@@ -731,8 +744,11 @@ def main():
                 t = time_calls(fn)
                 tag = "causal" if causal else "noncausal"
                 tf = fwd_flops(c.B, c.H, c.N, c.d, causal) / (t * 1e-3) / 1e12
+                roof = fwd_roof_tflops(c.B, c.H, c.N, c.d, causal)
                 row[f"{tag}_ms"] = round(t, 4)
                 row[f"{tag}_tflops"] = round(tf, 2)
+                row[f"{tag}_roof_tflops"] = round(roof, 1)
+                row[f"{tag}_frac_roof"] = round(tf / roof, 4)
                 if with_cpu:
                     modes[causal] = tuple(np.stack([x[b, h] for b, h in heads]) for x in host) + (
                         np.stack([os_[b, h].index_select(0, prow_d).float().cpu().numpy()

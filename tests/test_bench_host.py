@@ -37,6 +37,18 @@ def test_forward_flops_count_visible_pairs():
         assert b.bwd_flops(1, 1, N, 8, True) == 2.5 * b.fwd_flops(1, 1, N, 8, True)
 
 
+def test_forward_roof_is_hbm_bound_only_for_short_causal_rows():
+    b = _bench()
+    # bytes: q, k, v, o of every row at 2 bytes, one fp32 log-sum-exp per row
+    assert b.fwd_bytes(2, 3, 5, 16) == 2 * 3 * 5 * (4 * 16 * 2 + 4)
+    # the d=64 sweep at N=512, causal: 127 flop per byte, 8 TB/s below 2.5 PFLOP/s
+    roof = b.fwd_roof_tflops(32, 32, 512, 64, True)
+    inten = b.fwd_flops(32, 32, 512, 64, True) / b.fwd_bytes(32, 32, 512, 64)
+    assert 120 < inten < 130 and abs(roof - b.PEAK_HBM_GBS * inten / 1e3) < 1e-6
+    # long rows: the matrix peak
+    assert b.fwd_roof_tflops(8, 16, 2048, 128, False) == b.PEAK_BF16_TFLOPS
+
+
 def test_prefill_flops_count_visible_pairs():
     b = _bench()
     wl = w.prefill_workload(5, S=4, H=2, d=8, ctx_lens=[0, 3, 20, 1], new_lens=[5, 1, 7, 40],
