@@ -114,34 +114,47 @@ struct PagedKV {
     int64_t head_off;                          // elements to this head inside a page (h * 16 * D)
     int len;                                   // keys (cached tokens of the sequence)
     int gofs[FwdShape<D>::LPW];                // byte offset inside this wave's page, per load
+    int n_pages;
+    int sub;                                   // lane % 4
+    // The table entries of the tile load_k loads next, read one call ahead:
+    // lane l holds entry 4 kt + l % 4.  A vector load, so that the wait for it
+    // is the vmcnt(0) a tile already waits for its K/V loads (a scalar load
+    // would be waited with every LDS read of the tile).  Entries past the
+    // sequence's last page read that page's entry again (in bounds) and are
+    // not used.
+    int32_t nidv;
 
+    __device__ __forceinline__ void prefetch(int kt) {
+        const int last = max(n_pages - 1, 0);
+        nidv = table[min(4 * kt + sub, last)];
+    }
     __device__ __forceinline__ void setup(int wave, int lane) {
 #pragma unroll
         for (int i = 0; i < FwdShape<D>::LPW; ++i)
             gofs[i] = tile_load_offset<D>(wave * FwdShape<D>::LPW + i, lane) - wave * kPage * D * 2;
-    }
-    // Physical page of logical page p, or -1 when p is past the sequence or
-    // the entry is out of range (wave-uniform: scalar loads).
-    __device__ __forceinline__ int64_t page(int p) const {
-        const int n_pages = (len + kPage - 1) / kPage;
-        if (p >= n_pages) return -1;
-        const int64_t id = table[p];
-        return (id >= 0 && id < num_blocks) ? id : -1;
+        n_pages = (len + kPage - 1) / kPage;
+        sub = lane & 3;
+        prefetch(0);
     }
     int64_t cur_off = 0;                       // this wave's page of the tile being loaded
     int cur_bytes = 0;
+    // Issue tile kt's K loads (kt: 0, then each tile after the one before).
+    // Logical page 4 kt + w of the tile is the entry in lane w of nidv; a
+    // page past the sequence is not loaded, and one whose entry lies outside
+    // [0, num_blocks) is not followed and is reported in the returned mask.
     __device__ __forceinline__ uint32_t load_k(int kt, uint16_t* stage, int wave) {
         constexpr int LPW = FwdShape<D>::LPW;
-        const int n_pages = (len + kPage - 1) / kPage;
         uint32_t hide = 0u;
         int64_t mine = -1;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const int p = 4 * kt + w;
-            const int64_t id = page(p);
-            if (p < n_pages && id < 0) hide |= 1u << w;
-            if (w == wave) mine = id;
+            const int64_t raw = __builtin_amdgcn_readlane(nidv, w);
+            const bool ok = p < n_pages && raw >= 0 && raw < num_blocks;
+            if (p < n_pages && !ok) hide |= 1u << w;
+            if (w == wave) mine = ok ? raw : -1;
         }
+        prefetch(kt + 1);
         const int rows = (mine < 0) ? 0 : min(kPage, len - (4 * kt + wave) * kPage);
         cur_off = (mine < 0 ? 0 : mine) * page_stride + head_off;
         cur_bytes = rows * D * 2;

@@ -22,6 +22,64 @@ namespace {
 
 using namespace fa_gfx950;
 
+// Batches of up to this many sequences are taken heaviest first.
+constexpr int kSortedSeqs = kFwdThreads;
+
+// The sequence of rank t among the S <= kSortedSeqs sequences ordered by
+// decreasing work of their new rows (ties: lower index first): the
+// (query, key) pairs they see, n (2L - n + 1) / 2 under the causal mask, n L
+// without, for n new and L cached tokens.  Computed by every work group for
+// itself; called by all threads of the group.
+template <bool CAUSAL>
+__device__ __forceinline__ int seq_by_work_rank(const int32_t* __restrict__ seq_lens,
+                                                const int32_t* __restrict__ cu_q, int S,
+                                                int max_len, int t, float* key_sh, int* pick) {
+    const int i = threadIdx.x;
+    float key = 0.f;
+    if (i < S) {
+        const float L = (float)max(0, min(seq_lens[i], max_len));
+        const float n = (float)min(max(0, cu_q[i + 1] - cu_q[i]), max_len);
+        key = CAUSAL ? n * (2.f * L - n + 1.f) : n * L;
+        key_sh[i] = key;
+    }
+    __syncthreads();
+    if (i < S) {
+        int rank = 0;
+        for (int j = 0; j < S; ++j) {
+            const float v = key_sh[j];
+            rank += (v > key || (v == key && j < i)) ? 1 : 0;
+        }
+        if (rank == t) *pick = i;
+    }
+    __syncthreads();
+    return *pick;
+}
+
+// The sequence of rank t among the S <= kSortedSeqs sequences ordered by
+// decreasing cached length (ties: lower index first), computed by every work
+// group for itself: thread i reads sequence i's length and counts the
+// sequences ahead of it.  Called by all threads of the group.
+__device__ __forceinline__ int seq_by_length_rank(const int32_t* __restrict__ seq_lens, int S,
+                                                  int max_len, int t, int* len_sh, int* pick) {
+    const int i = threadIdx.x;
+    int len = 0;
+    if (i < S) {
+        len = max(0, min(seq_lens[i], max_len));
+        len_sh[i] = len;
+    }
+    __syncthreads();
+    if (i < S) {
+        int rank = 0;
+        for (int j = 0; j < S; ++j) {
+            const int v = len_sh[j];
+            rank += (v > len || (v == len && j < i)) ? 1 : 0;
+        }
+        if (rank == t) *pick = i;
+    }
+    __syncthreads();
+    return *pick;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 2)
 void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
@@ -34,18 +92,27 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * FwdShape<D>::TILE];
 
     // work group -> (sequence, head, query block).  Work groups are dealt to
-    // the 8 XCDs round-robin (XCD = blockIdx % 8).  Unit u = (sequence u / H,
-    // head u % H) goes to XCD u % 8, its query blocks one after another there
-    // (they share the unit's K/V through that XCD's L2); so every XCD gets
-    // the same share of every sequence, however unequal the sequences are.
-    // Causal: longest rows first.
+    // the 8 XCDs round-robin (XCD = blockIdx % 8).  Unit u = (sequence of
+    // rank u / H, head u % H) goes to XCD u % 8, its query blocks one after
+    // another there (they share the unit's K/V through that XCD's L2); so
+    // every XCD gets the same share of every sequence, however unequal the
+    // sequences are.  The sequences come heaviest first (up to kSortedSeqs of
+    // them), so that no long one is left for the end of the grid; causal:
+    // longest rows first within a unit.
+    __shared__ float key_sh[kSortedSeqs];
+    __shared__ int pick;
     const int x = blockIdx.x & 7;
     const int k = blockIdx.x >> 3;             // k-th work group on XCD x
     const int j = k / n_qblocks;
     const int u = 8 * j + x;
     if (u >= n_units) return;                  // padding of the grid
-    const int s = u / H;
-    const int h = u - s * H;
+    const int t = u / H;
+    const int h = u - t * H;
+    const int n_seq = n_units / H;
+    const int s = (n_seq <= kSortedSeqs)
+                      ? seq_by_work_rank<CAUSAL>(seq_lens, cu_q, n_seq,
+                                                 max_blocks * PagedKV<D>::kPage, t, key_sh, &pick)
+                      : t;
     int qb = k - j * n_qblocks;
     if (CAUSAL) qb = n_qblocks - 1 - qb;
 
@@ -78,34 +145,6 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // the new tokens are the last n_new of the L cached ones; row r stands at
     // position L - n_new + r whether or not later rows are computed
     fwd_block<D, CAUSAL>(smem0, smem1, qr, kv, q0, L - n_new, scale_log2);
-}
-
-// Batches of up to this many sequences are verified longest first.
-constexpr int kSortedSeqs = kFwdThreads;
-
-// The sequence of rank t among the S <= kSortedSeqs sequences ordered by
-// decreasing cached length (ties: lower index first), computed by every work
-// group for itself: thread i reads sequence i's length and counts the
-// sequences ahead of it.  Called by all threads of the group.
-__device__ __forceinline__ int seq_by_length_rank(const int32_t* __restrict__ seq_lens, int S,
-                                                  int max_len, int t, int* len_sh, int* pick) {
-    const int i = threadIdx.x;
-    int len = 0;
-    if (i < S) {
-        len = max(0, min(seq_lens[i], max_len));
-        len_sh[i] = len;
-    }
-    __syncthreads();
-    if (i < S) {
-        int rank = 0;
-        for (int j = 0; j < S; ++j) {
-            const int v = len_sh[j];
-            rank += (v > len || (v == len && j < i)) ? 1 : 0;
-        }
-        if (rank == t) *pick = i;
-    }
-    __syncthreads();
-    return *pick;
 }
 
 // Draft-tree verification ("LLM study notes", speculative decoding section:
