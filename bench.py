@@ -349,7 +349,7 @@ def main():
                     help="do not time the plain bf16 GEMM (the MFMA throughput the vendor BLAS "
                          "reaches on this GPU, reported next to the attention figures)")
     ap.add_argument("--only", choices=["fwd-noncausal", "fwd-causal", "decode", "bwd-noncausal",
-                                       "bwd-causal", "prefill", "tree", "rope", "gemm"],
+                                       "bwd-causal", "prefill", "tree", "rope", "gemm", "sweep"],
                     help="run one call per step (for per-kernel counter runs)")
     ap.add_argument("--probe-copy", type=int, metavar="MIB",
                     help="instead of the hot path, copy a buffer of MIB MiB a few times "
@@ -723,7 +723,7 @@ def main():
     # ---- the other forward configurations: the sequence sweep at 16k tokens
     #      (H=32, d=64) and the long-context one (B=1 H=16 N=16384 d=128,
     #      causal, q and k with standard deviation 3), on their seeded inputs
-    if not args.skip_sweep and args.only is None:
+    if not args.skip_sweep and args.only in (None, "sweep"):
         out["sweep"] = {}
         samples["sweep"] = {}
         for name, c in w.FWD_CONFIGS.items():
@@ -841,6 +841,9 @@ def main():
         del buf, order, sink
         log("read probe timed")
 
+    if args.only == "sweep":
+        print(json.dumps({"only": "sweep", "sweep": out["sweep"]}), flush=True)
+        return
     if args.only is not None:
         ms = {"fwd-noncausal": t_nc, "fwd-causal": t_c, "decode": t_dec,
               "bwd-noncausal": t_bwd.get(False), "bwd-causal": t_bwd.get(True),
