@@ -93,8 +93,9 @@ void fwd_bf16_persist_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t ost[8 * kOStageBytes / 2];
     fwd_pingpong_persistent<D, CAUSAL, false>(kb0, kb1, vb0, vb1, Q, K, V, O, LSE, N,
-                                              n_qblocks, total_units, scale_log2);
+                                              n_qblocks, total_units, scale_log2, ost);
 }
 
 }  // namespace

@@ -114,8 +114,9 @@ void fwd_rope_persist_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     __shared__ __attribute__((aligned(1024))) uint16_t kb1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t vb1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t ost[8 * kOStageBytes / 2];
     fwd_pingpong_persistent<D, CAUSAL, true>(kb0, kb1, vb0, vb1, Q, K, V, O, LSE, N, n_qblocks,
-                                             total_units, scale_log2, rope_cos, rope_sin);
+                                             total_units, scale_log2, ost, rope_cos, rope_sin);
 }
 
 template <int D>
