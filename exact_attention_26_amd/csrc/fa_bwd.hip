@@ -343,22 +343,8 @@ __device__ __forceinline__ void dkdv1_block(uint16_t* smem0, uint16_t* smem1,
     if (qt < n_qt) tile_step(qt++, stage1, stage0, Mask{});
 
     // epilogue: lane holds key `key`, d = db*32 + 8i + 4g + j in register 4i + j
-    if (key < N) {
-        uint16_t* dvrow = dV + base + (size_t)key * D;
-        uint16_t* dkrow = dK + base + (size_t)key * D;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = db * 32 + 8 * i + 4 * g;
-                *reinterpret_cast<bf16x4*>(dvrow + col) =
-                    to_bf16x4(dvacc[db][4 * i], dvacc[db][4 * i + 1], dvacc[db][4 * i + 2],
-                              dvacc[db][4 * i + 3]);
-                *reinterpret_cast<bf16x4*>(dkrow + col) =
-                    to_bf16x4(scale * dkacc[db][4 * i], scale * dkacc[db][4 * i + 1],
-                              scale * dkacc[db][4 * i + 2], scale * dkacc[db][4 * i + 3]);
-            }
-    }
+    store_o_row<ND>(dV + base + (size_t)key * D, dvacc, 1.f, g, key < N);
+    store_o_row<ND>(dK + base + (size_t)key * D, dkacc, scale, g, key < N);
 }
 
 // ---------------------------------------------------------------------------
@@ -722,17 +708,8 @@ __device__ __forceinline__ void dkdv_block(uint16_t* st0, uint16_t* st1, uint16_
     __builtin_amdgcn_s_waitcnt(0x0F70);        // the last (repeated) loads have landed
 
     // epilogue: lane holds key `key`, d = db*32 + 8i + 4g + j in register 4i + j
-    if (key < N) {
-        uint16_t* row = (pwave ? dV : dK) + base + (size_t)key * D;
-        const float f = pwave ? 1.f : scale;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<bf16x4*>(row + db * 32 + 8 * i + 4 * g) =
-                    to_bf16x4(f * acc[db][4 * i], f * acc[db][4 * i + 1], f * acc[db][4 * i + 2],
-                              f * acc[db][4 * i + 3]);
-    }
+    store_o_row<ND>((pwave ? dV : dK) + base + (size_t)key * D, acc, pwave ? 1.f : scale, g,
+                    key < N);
 }
 
 // Causal work balance (both gradient kernels): under the causal mask key
@@ -943,16 +920,7 @@ __device__ __forceinline__ void dq_block(uint16_t* smem0, uint16_t* smem1,
         if (kt + 1 < n_kt) tile_step(kt + 1, stage1, stage0, Mask{});
     }
 
-    if (qrow < N) {
-        uint16_t* dqrow = dQ + base + (size_t)qrow * D;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<bf16x4*>(dqrow + db * 32 + 8 * i + 4 * g) =
-                    to_bf16x4(scale * dqacc[db][4 * i], scale * dqacc[db][4 * i + 1],
-                              scale * dqacc[db][4 * i + 2], scale * dqacc[db][4 * i + 3]);
-    }
+    store_o_row<ND>(dQ + base + (size_t)qrow * D, dqacc, scale, g, qrow < N);
 }
 
 template <int D, bool CAUSAL>

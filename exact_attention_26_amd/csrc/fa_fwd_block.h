@@ -287,40 +287,6 @@ __device__ __forceinline__ void score_mfmas(f32x16 (&sacc)[2], const uint16_t* k
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-// Row `orow` of O from a lane's O^T accumulators (oacc[db][4j + i] holds
-// column db*32 + 8j + 4g + i), times inv, as bf16 with 16-byte stores: lanes
-// l and l + 32 hold the two halves of each 16-column group of row l and swap
-// pieces with v_permlane32_swap, so that each then holds 8 consecutive
-// columns (half as many store instructions as 8-byte stores of the pieces as
-// they are, measured 2-4 % faster in the forwards).  Every lane must run it
-// (the swap reads the partner lane); `store` false skips only the stores.
-template <int ND>
-__device__ __forceinline__ void store_o_row(uint16_t* orow, const f32x16 (&oacc)[ND], float inv,
-                                            int g, bool store) {
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-            u32x2 a = __builtin_bit_cast(
-                u32x2, to_bf16x4(oacc[db][8 * pr] * inv, oacc[db][8 * pr + 1] * inv,
-                                 oacc[db][8 * pr + 2] * inv, oacc[db][8 * pr + 3] * inv));
-            u32x2 b = __builtin_bit_cast(
-                u32x2, to_bf16x4(oacc[db][8 * pr + 4] * inv, oacc[db][8 * pr + 5] * inv,
-                                 oacc[db][8 * pr + 6] * inv, oacc[db][8 * pr + 7] * inv));
-            // lane l keeps a (columns 16pr .. +3 of its group) and takes the
-            // partner's a (+4 .. +7); lane l + 32 takes the partner's b
-            // (+8 .. +11) and keeps its own b (+12 .. +15)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const auto r = __builtin_amdgcn_permlane32_swap(a[h], b[h], false, false);
-                a[h] = r[0];
-                b[h] = r[1];
-            }
-            const u32x4 w = {a[0], a[1], b[0], b[1]};
-            if (store) *reinterpret_cast<u32x4*>(orow + db * 32 + 16 * pr + 8 * g) = w;
-        }
-}
-
 // Query fragments of one lane: row qrow, elements kc*16 + 8g .. +8 for every
 // kc, as the B operand of S^T = K Q^T, sign bits flipped by qflip (a negative
 // scale); rows past qr.rows are zero.  Branch-free: such rows load the last

@@ -155,6 +155,41 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
     return w;
 }
 
+// One output row (O, or dQ / dK / dV) from a lane's transposed MFMA
+// accumulators (oacc[db][4j + i] holds column db*32 + 8j + 4g + i of the
+// lane's row), times inv, as bf16 with 16-byte stores: lanes l and l + 32
+// hold the two halves of each 16-column group of row l and swap pieces with
+// v_permlane32_swap, so that each then holds 8 consecutive columns (half as
+// many store instructions as 8-byte stores of the pieces as they are,
+// measured 2-4 % faster in the forwards).  Every lane must run it
+// (the swap reads the partner lane); `store` false skips only the stores.
+template <int ND>
+__device__ __forceinline__ void store_o_row(uint16_t* orow, const f32x16 (&oacc)[ND], float inv,
+                                            int g, bool store) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            u32x2 a = __builtin_bit_cast(
+                u32x2, to_bf16x4(oacc[db][8 * pr] * inv, oacc[db][8 * pr + 1] * inv,
+                                 oacc[db][8 * pr + 2] * inv, oacc[db][8 * pr + 3] * inv));
+            u32x2 b = __builtin_bit_cast(
+                u32x2, to_bf16x4(oacc[db][8 * pr + 4] * inv, oacc[db][8 * pr + 5] * inv,
+                                 oacc[db][8 * pr + 6] * inv, oacc[db][8 * pr + 7] * inv));
+            // lane l keeps a (columns 16pr .. +3 of its group) and takes the
+            // partner's a (+4 .. +7); lane l + 32 takes the partner's b
+            // (+8 .. +11) and keeps its own b (+12 .. +15)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const auto r = __builtin_amdgcn_permlane32_swap(a[h], b[h], false, false);
+                a[h] = r[0];
+                b[h] = r[1];
+            }
+            const u32x4 w = {a[0], a[1], b[0], b[1]};
+            if (store) *reinterpret_cast<u32x4*>(orow + db * 32 + 16 * pr + 8 * g) = w;
+        }
+}
+
 // Rotate the four complex numbers (x[2i] + j x[2i+1], i = 0..3) held as 8
 // bf16 in x by the angles whose cosines / sines are c, s: fp32 arithmetic,
 // results rounded to nearest even bf16.
