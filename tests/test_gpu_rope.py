@@ -106,6 +106,31 @@ def test_fwd_rope_negative_scale(gpu_device):
                      to_host(lse))
 
 
+def test_fwd_rope_stream_edges(gpu_device):
+    """d = 128, N a multiple of 64 from 704 up (the persistent stream): N not
+    a multiple of the 256-row block (rows past N in the last block of every
+    head), a negative scale, several blocks per work group; against the
+    oracle and bitwise against fa_rope(q), fa_rope(k), fa_fwd."""
+    import torch
+    d = 128
+    for (B, H, n, scale) in ((1, 3, 960, -0.2), (2, 2, 1088, 1 / math.sqrt(d))):
+        q, k, v = w.fwd_inputs(B, H, n, d, seed=977 + n)
+        c, s, cd, sd = _tables(n, d, gpu_device)
+        qd, kd, vd = (to_dev(x, "bf16", gpu_device) for x in (q, k, v))
+        rows = np.array([0, 1, 255, 256, 511, 700, n - 65, n - 64, n - 2, n - 1])
+        for causal in (False, True):
+            say(f"fwd_rope stream B={B} H={H} N={n} scale={scale:.3f} causal={causal}")
+            o, lse = fa.attention_rope(qd, kd, vd, cd, sd, causal=causal, scale=scale)
+            uo, ul = fa.attention(fa.rope(qd, cd, sd), fa.rope(kd, cd, sd), vd, causal=causal,
+                                  scale=scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o, uo) and torch.equal(lse, ul)
+            for b, h in ((0, 0), (B - 1, H - 1)):
+                _check_fused(f"N={n} b={b} h={h} causal={causal}", q[b, h], k[b, h], v[b, h],
+                             c, s, causal, scale, to_host(o[b, h, rows]),
+                             to_host(lse[b, h, rows]), rows=rows)
+
+
 def test_fwd_rope_full_size_and_matches_unfused(gpu_device):
     """The forward bench workload (B=8 H=16 N=2048 d=128) with RoPE: sampled
     rows against the oracle; and the fused call gives the same bits as
