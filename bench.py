@@ -608,7 +608,7 @@ def main():
                                f"{tag}_frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         out["bwd"]["flops"] = "2.5x forward (10 N^2 d per head non-causal)"
         out["bwd"]["traffic"] = {k: measured_traffic(f"{k} B=8 H=16 N=2048") for k in (
-            "bwd_dkdv_kernel<128,false>", "bwd_dq_kernel<128,false>", "bwd_prep_kernel<128>")}
+            "bwd_dkdv_kernel<128,false>", "bwd_dq_kernel<128,false>")}
 
     # ---- paged prefill, its own timed loop ----
     t_pre = None

@@ -11,9 +11,14 @@
 //     dQ = scale dS K,   dK = scale dS^T Q
 // (delta_i equals sum_j P_ij dP_ij: the softmax Jacobian's row term).
 //
-// Three launches, no atomics, so results are deterministic:
-//  1. bwd_prep_kernel: per 32-row block of a head, lse2 = LSE log2(e) and
-//     delta, into a small workspace (256 bytes per block: one LDS DMA load).
+// Two launches, no atomics, so results are deterministic:
+//  1. bwd_dq_kernel: a work group owns 128 queries (32 per wave, Q and dO rows
+//     in registers) and streams K / V tiles, as the forward does: S^T = K Q^T,
+//     dP^T = V dO^T (lane = one query, so lse2 and delta are per-lane scalars),
+//     dS^T in registers, dQ^T += K^T dS^T.  Its prologue forms each row's
+//     statistics, lse2 = LSE log2(e) and delta, from the dO fragments it holds
+//     and the O row, and stores them per 32-row block into a small workspace
+//     (256 bytes per block: one LDS DMA load for the next kernel).
 //  2. dK and dV: a work group owns 128 keys and streams the Q / dO rows
 //     through LDS (HBM -> LDS without registers), in one of two layouts:
 //     bwd_dkdv_kernel (d = 128): each 32-key slice is worked by a pair of
@@ -23,11 +28,7 @@
 //     bwd_dkdv1_kernel (d = 64): one wave per slice does all four products
 //     (small enough at d = 64 for two waves per SIMD).  Transposed operands
 //     are read by ds_read_b64_tr_b16.
-//  3. bwd_dq_kernel: a work group owns 128 queries (32 per wave, Q and dO rows
-//     in registers) and streams K / V tiles, as the forward does: S^T = K Q^T,
-//     dP^T = V dO^T (lane = one query, so lse2 and delta are per-lane scalars),
-//     dS^T in registers, dQ^T += K^T dS^T.
-// Recomputing S and dP in both (2) and (3) costs 14 N^2 d flops per head
+// Recomputing S and dP in both (1) and (2) costs 14 N^2 d flops per head
 // instead of 10 N^2 d, the price of having no atomic dQ accumulation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,7 +45,7 @@ using namespace fa_gfx950;
 
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int BQ = 64;                 // query rows per work group of the statistics kernel
+constexpr int BQ = 64;                 // query rows per Q / dO tile of the one-wave dK/dV kernel
 constexpr int BKV = 64;                // key rows per tile in the dQ kernel
 constexpr int BM = NWAVES * 32;        // queries per dQ work group
 constexpr int BK = 128;                // keys per dK/dV work group
@@ -52,51 +53,6 @@ constexpr int SB = 32;                 // query rows per statistics block
 constexpr int SB_FLOATS = 2 * SB;      // per 32-row block: lse2[32], delta[32] (256 bytes)
 
 // ---------------------------------------------------------------------------
-// 1. Row statistics.  One work group per (b*h, 64 rows); four lanes per row,
-//    each summing a quarter of dO_i . O_i in fp32.  Stored per 32-row block
-//    (256 bytes: lse2 of its rows, then delta), the unit the dK/dV kernel
-//    loads with one buffer -> LDS instruction.  Rows past N get
-//    lse2 = delta = 0, which makes the padded rows of the last Q / dO block
-//    contribute exactly zero (their Q and dO rows are zero as well).
-template <int D>
-__global__ __launch_bounds__(NTHREADS)
-void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                     const float* __restrict__ LSE, float* __restrict__ stats, int N, int n_tiles,
-                     int n_sb) {
-    constexpr int PART = D / 4;                // elements per lane
-    const int wg = blockIdx.x;
-    const int bh = wg / n_tiles;
-    const int t = wg - bh * n_tiles;
-    const int r = threadIdx.x >> 2;
-    const int part = threadIdx.x & 3;
-    const int row = t * BQ + r;
-    float dot = 0.f, l2 = 0.f;
-    if (row < N) {
-        const size_t off = ((size_t)bh * N + row) * D + part * PART;
-        const u32x4* op = reinterpret_cast<const u32x4*>(O + off);
-        const u32x4* gp = reinterpret_cast<const u32x4*>(dO + off);
-#pragma unroll
-        for (int c = 0; c < PART / 8; ++c) {
-            const u32x4 a = op[c];
-            const u32x4 b = gp[c];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                dot = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), dot);
-                dot = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(b[w] & 0xFFFF0000u), dot);
-            }
-        }
-        l2 = LSE[(size_t)bh * N + row] * kLog2e;
-    }
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
-    const int blk = row / SB;
-    if (part == 0 && blk < n_sb) {
-        float* st = stats + ((size_t)bh * n_sb + blk) * SB_FLOATS;
-        st[row % SB] = l2;
-        st[SB + row % SB] = dot;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // 2a. dK, dV at d = 64: one wave per key slice.
 //
@@ -789,7 +745,9 @@ __device__ __forceinline__ void dq_block(uint16_t* smem0, uint16_t* smem1,
                                          const uint16_t* __restrict__ K,
                                          const uint16_t* __restrict__ V,
                                          const uint16_t* __restrict__ dO,
-                                         const float* __restrict__ stats,
+                                         const uint16_t* __restrict__ O,
+                                         const float* __restrict__ LSE,
+                                         float* __restrict__ stats,
                                          uint16_t* __restrict__ dQ, int N, float scale_log2,
                                          float scale, int bh, int q0) {
     constexpr int TILE = BKV * D;
@@ -813,12 +771,14 @@ __device__ __forceinline__ void dq_block(uint16_t* smem0, uint16_t* smem1,
         qop[kc] = row_operand<D>(Q + base, qrow, N, 2 * kc + g, 0u);
         doop[kc] = row_operand<D>(dO + base, qrow, N, 2 * kc + g, 0u);
     }
+    // the row's statistics: lse2 = LSE log2(e) and delta = dO . O in fp32,
+    // formed once the first K / V tile is in flight (below)
     float lse2 = 0.f, delta = 0.f;
-    if (qrow < N) {
-        const float* st = stats + ((size_t)bh * ((N + SB - 1) / SB) + qrow / SB) * SB_FLOATS;
-        lse2 = st[qrow % SB];
-        delta = st[SB + qrow % SB];
-    }
+    u32x4 orow[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+        orow[kc] = __builtin_bit_cast(u32x4, row_operand<D>(O + base, qrow, N, 2 * kc + g, 0u));
+    const float lse_row = LSE[(size_t)bh * N + min(qrow, N - 1)];   // used for rows < N only
     f32x16 dqacc[ND];
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -908,6 +868,36 @@ __device__ __forceinline__ void dq_block(uint16_t* smem0, uint16_t* smem1,
     uint16_t* const stage0 = smem0;
     uint16_t* const stage1 = smem1;
     load_tile(0, stage0);
+    {
+        // each lane sums the half of the row its dO fragments hold (elements
+        // kc*16 + 8g .. +8), lane l + 32 the other half.  Stored per 32-row
+        // block (lse2 of its rows, then delta) for the dK/dV kernel, which
+        // runs after this one; rows past N get lse2 = delta = 0, which makes
+        // the padded rows of the last Q / dO block contribute exactly zero
+        // there (their Q and dO rows are zero as well).
+        float dot = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            const u32x4 b = __builtin_bit_cast(u32x4, doop[kc]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                dot = fmaf(__uint_as_float(orow[kc][w] << 16), __uint_as_float(b[w] << 16), dot);
+                dot = fmaf(__uint_as_float(orow[kc][w] & 0xFFFF0000u),
+                           __uint_as_float(b[w] & 0xFFFF0000u), dot);
+            }
+        }
+        dot += __shfl_xor(dot, 32);
+        if (qrow < N) {
+            lse2 = lse_row * kLog2e;
+            delta = dot;
+        }
+        const int n_sb = (N + SB - 1) / SB;
+        if (g == 0 && qrow / SB < n_sb) {
+            float* st = stats + ((size_t)bh * n_sb + qrow / SB) * SB_FLOATS;
+            st[qrow % SB] = lse2;
+            st[SB + qrow % SB] = delta;
+        }
+    }
     int kt = 0;
     for (; kt < n_full; kt += 2) {
         tile_step(kt, stage0, stage1, NoMask{});
@@ -927,7 +917,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                   const float* __restrict__ stats, uint16_t* __restrict__ dQ, int N,
+                   const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+                   float* __restrict__ stats, uint16_t* __restrict__ dQ, int N,
                    int n_qblocks, float scale_log2, float scale) {
     // two stages (K tile, V tile), separate arrays as in the dK/dV kernel
     __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * BKV * D];
@@ -944,8 +935,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int n_blocks = (CAUSAL && p < first) ? 2 : 1;
     for (int i = 0; i < n_blocks; ++i) {
         if (i > 0) __syncthreads();            // the first block's last tile is read
-        dq_block<D, CAUSAL>(smem0, smem1, Q, K, V, dO, stats, dQ, N, scale_log2, scale, bh,
-                            (i == 0 ? first : p) * BM);
+        dq_block<D, CAUSAL>(smem0, smem1, Q, K, V, dO, O, LSE, stats, dQ, N, scale_log2, scale,
+                            bh, (i == 0 ? first : p) * BM);
     }
 }
 
@@ -966,29 +957,23 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     float scale_log2 = (float)((double)scale * 1.4426950408889634074);
     const unsigned bh = (unsigned)B * (unsigned)H;
 
-    int n_tiles = (N + BQ - 1) / BQ;
-    int n_sb = (N + SB - 1) / SB;
-    void* a1[] = {&op, &gp, &lp, &stats, &N, &n_tiles, &n_sb};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_kernel<D>),
-                                   dim3(bh * (unsigned)n_tiles), dim3(NTHREADS), a1, 0, stream);
+    // dQ first: its prologue stores the row statistics the dK/dV kernel reads
+    int n_qblocks = (N + BM - 1) / BM;
+    const unsigned g3 = (unsigned)(CAUSAL ? causal_groups(n_qblocks) : n_qblocks);
+    void* a3[] = {&qp, &kp, &vp, &gp, &op, &lp, &stats, &dqp, &N, &n_qblocks, &scale_log2, &scale};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL>),
+                                   dim3(bh * g3), dim3(NTHREADS), a3, 0, stream);
     if (e != hipSuccess) return e;
 
     int n_kblocks = (N + BK - 1) / BK;
     const unsigned g2 = (unsigned)(CAUSAL ? causal_groups(n_kblocks) : n_kblocks);
     void* a2[] = {&qp, &kp, &vp, &gp, &sp, &dkp, &dvp, &N, &n_kblocks, &scale_log2, &scale};
     if constexpr (D == 64)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv1_kernel<D, CAUSAL>),
-                            dim3(bh * g2), dim3(NTHREADS), a2, 0, stream);
+        return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv1_kernel<D, CAUSAL>),
+                               dim3(bh * g2), dim3(NTHREADS), a2, 0, stream);
     else
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL>),
-                            dim3(bh * g2), dim3(DKDV_THREADS), a2, 0, stream);
-    if (e != hipSuccess) return e;
-
-    int n_qblocks = (N + BM - 1) / BM;
-    const unsigned g3 = (unsigned)(CAUSAL ? causal_groups(n_qblocks) : n_qblocks);
-    void* a3[] = {&qp, &kp, &vp, &gp, &sp, &dqp, &N, &n_qblocks, &scale_log2, &scale};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D, CAUSAL>),
-                           dim3(bh * g3), dim3(NTHREADS), a3, 0, stream);
+        return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL>),
+                               dim3(bh * g2), dim3(DKDV_THREADS), a2, 0, stream);
 }
 
 }  // namespace
