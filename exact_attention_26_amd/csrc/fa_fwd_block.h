@@ -369,6 +369,15 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
     }
     n_full = min(n_full, n_kt);
 
+    // ---- tree mode: the parent indices of the (at most kMaxTreeNodes)
+    //      nodes are loaded first, one per lane of the first wave, and staged
+    //      in LDS below, so that each row's walk up its path reads LDS rather
+    //      than waiting on one global load per step
+    int par_mine = -1;
+    if constexpr (TREE) {
+        if (threadIdx.x < qr.rows && threadIdx.x < kMaxTreeNodes) par_mine = parents[threadIdx.x];
+    }
+
     // ---- the first K/V tile's HBM -> LDS loads go out before anything else,
     //      so their latency overlaps the query loads below
     kv.setup(wave, lane);
@@ -393,14 +402,20 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
     //      and its ancestors; the walk ends because parents precede children)
     uint64_t path = 0;
     if constexpr (TREE) {
+        __shared__ int par_lds[kMaxTreeNodes];
+        if (threadIdx.x < kMaxTreeNodes) par_lds[threadIdx.x] = par_mine;
+        // the LDS writes are visible to every wave after this barrier; the
+        // tile and query loads in flight are not waited for
+        __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
         if (qrow < qr.rows && qrow < kMaxTreeNodes) {
             path = 1ull << qrow;
             int cur = qrow;
-            int p = parents[qrow];
+            int p = par_lds[qrow];
             while (p >= 0 && p < cur) {
                 path |= 1ull << p;
                 cur = p;
-                p = parents[p];
+                p = par_lds[p];
             }
         }
     }
