@@ -405,9 +405,13 @@ __device__ __forceinline__ void fwd_block(uint16_t* smem0, uint16_t* smem1, cons
         __shared__ int par_lds[kMaxTreeNodes];
         if (threadIdx.x < kMaxTreeNodes) par_lds[threadIdx.x] = par_mine;
         // the LDS writes are visible to every wave after this barrier; the
-        // tile and query loads in flight are not waited for
+        // tile and query loads in flight are not waited for (no fence: the
+        // empty asm statements keep the compiler from moving memory accesses
+        // across the barrier)
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         if (qrow < qr.rows && qrow < kMaxTreeNodes) {
             path = 1ull << qrow;
             int cur = qrow;
