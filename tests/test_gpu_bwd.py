@@ -110,6 +110,30 @@ def test_bwd_deterministic(gpu_device):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_workspace_contents_do_not_matter(gpu_device, d):
+    """The row statistics are written by the backward itself (rows past N of
+    the last 32-row block as zeros): a workspace full of NaN bytes gives the
+    same bits as a zeroed one; N = 300 leaves 20 padded rows in the last block."""
+    import torch
+    B, H, n = 1, 3, 300
+    q, k, v = w.fwd_inputs(B, H, n, d, seed=81)
+    do = w.bwd_dout(B, H, n, d, seed=81)
+    qd, kd, vd, dod = (to_dev(x, "bf16", gpu_device) for x in (q, k, v, do))
+    nbytes = fa.fa_bwd_workspace_size(B, H, n, d)
+    for causal in (False, True):
+        say(f"bwd workspace poison N={n} d={d} causal={causal}")
+        o, lse = fa.attention(qd, kd, vd, causal=causal)
+        ws0 = torch.zeros(nbytes, dtype=torch.uint8, device=gpu_device)
+        wsn = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=gpu_device)
+        a = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=causal, workspace=ws0)
+        b = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=causal, workspace=wsn)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+            assert torch.isfinite(x.float()).all()
+
+
 def test_bwd_rejections(gpu_device):
     import torch
     q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=gpu_device)
